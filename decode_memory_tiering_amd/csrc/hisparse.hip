@@ -1,0 +1,864 @@
+// hisparse.hip -- HiSparse decode-step swap-in resolver for MI355X (gfx950).
+//
+// Kernels (all wave64):
+//   swap_in_kernel   the fused resolver: resident / fast-path exit, LDS hash
+//                    hit detection, ballot-scan LRU compaction, victim
+//                    assignment, plan record and the miss copy from pinned
+//                    host memory, in one launch with one workgroup per
+//                    batch row.  SGLang guide "HiSparse: Hierarchical Sparse
+//                    Attention", "Decode Workflow"; vLLM design note "HiSparse
+//                    local KV offload architecture", "Resident device pages"
+//                    and "Hot lookup and LRU".
+//   replay_kernel    copy-only replay of a plan row on a skip layer, small
+//                    fixed grid.  SGLang guide, "Shared-index prefetch".
+//   backup_kernel    newest token's row, hot buffer -> host pool.  SGLang
+//                    guide, "Decode Workflow" (eager backup).
+//   store_newest_kernel, admit_*_kernel, init_state_kernel: the forward's KV
+//                    write, request admission, context set-up.
+//
+// Tie-breaks the pages leave open (same readings as the oracle, reached
+// independently here): victims come from the least-recent end of the LRU list
+// in order; misses take them in ascending top-k index; the reorder is stable
+// (new order = untouched non-hit slots, then hit slots, then loaded slots).
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "hisparse.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kMissMark = INT_MIN;   // out_s value of an entry still waiting for a victim
+constexpr int kMaxB = 16384;
+constexpr int kMaxK = 4096;
+constexpr int kDefaultBlock = 1024;
+constexpr int kDefaultReplayGrid = 32;
+constexpr int kCopyUnroll = 4;       // 16-byte loads in flight per thread in the copy loops
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+__device__ __forceinline__ uint32_t hash_slot(int32_t t, int bits)
+{
+    return (static_cast<uint32_t>(t) * 0x9E3779B1u) >> (32 - bits);
+}
+
+// Exclusive prefix sum, in place, of a[0..n) by one wave; returns the total to
+// every lane.
+__device__ int wave_exclusive_scan(int* a, int n)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int per = (n + kWave - 1) / kWave;
+    const int base = lane * per;
+    int own = 0;
+    for (int k = 0; k < per; ++k)
+        if (base + k < n) own += a[base + k];
+    int incl = own;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int y = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += y;
+    }
+    int run = incl - own;
+    for (int k = 0; k < per; ++k) {
+        if (base + k < n) {
+            int v = a[base + k];
+            a[base + k] = run;
+            run += v;
+        }
+    }
+    return __shfl(incl, kWave - 1, kWave);
+}
+
+// Copy `rows` rows of rb bytes (rb % 16 == 0) from src rows to dst rows, the
+// row numbers given by src_row(m) / dst_row(m); chunk c of the flattened
+// (row, 16-byte column) space goes to thread c % nthr.  kCopyUnroll loads are
+// issued before their stores so that enough host-link reads are in flight.
+template <typename SrcRow, typename DstRow>
+__device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                          int rows, int rb, int tid, int nthr,
+                                          SrcRow src_row, DstRow dst_row)
+{
+    const int cpr = rb >> 4;
+    const int total = rows * cpr;
+    if (tid >= total) return;
+    int row = tid / cpr, col = tid - (tid / cpr) * cpr;
+    const int drow = nthr / cpr, dcol = nthr - (nthr / cpr) * cpr;
+    for (int base = tid; base < total; base += kCopyUnroll * nthr) {
+        u32x4 v[kCopyUnroll];
+        int rr[kCopyUnroll], cc[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            rr[u] = row;
+            cc[u] = col;
+            if (base + u * nthr < total) {
+                const u32x4* p = reinterpret_cast<const u32x4*>(
+                    src + static_cast<size_t>(src_row(row)) * rb + (static_cast<size_t>(col) << 4));
+                v[u] = __builtin_nontemporal_load(p);
+            }
+            col += dcol;
+            row += drow;
+            if (col >= cpr) { col -= cpr; ++row; }
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            if (base + u * nthr < total) {
+                u32x4* q = reinterpret_cast<u32x4*>(
+                    dst + static_cast<size_t>(dst_row(rr[u])) * rb + (static_cast<size_t>(cc[u]) << 4));
+                *q = v[u];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the fused resolver
+// ---------------------------------------------------------------------------
+struct SwapInArgs {
+    const int32_t* topk;         // [nb][K]
+    const int32_t* seq_lens;     // [nb]
+    const uint8_t* resident;     // [nb] or null
+    const int32_t* req_idx;      // [nb] or null
+    int32_t* out;                // [nb][K]
+    int32_t* plan_pos;           // [nb][K]
+    int32_t* plan_slot;          // [nb][K]
+    int32_t* plan_count;         // [nb]
+    int32_t* lru;                // [R][B]  least recent first
+    int32_t* tok;                // [R][B]  position held by each slot, -1 = empty
+    const uint8_t* host;         // [R][max_seq][rb]
+    uint8_t* hot;                // [R][B+1][rb]
+    uint32_t* err;
+    int32_t R, B, K, rb, max_seq, hash_bits;
+};
+
+struct SwapInLds {
+    int* hash;      // [1 << hash_bits]  top-k index of a candidate position, -1 empty
+    int* topk_s;    // [K]
+    int* out_s;     // [K]   -1 / B / slot of a hit / kMissMark
+    int* plan_t;    // [K]   m-th miss: host position
+    int* plan_v;    // [K]   m-th least recent non-hit slot (victim of the m-th miss)
+    int* cnt_b;     // [ceil(B/64)]  hits per 64-entry chunk of the LRU list, then prefix
+    int* cnt_k;     // [ceil(K/64)]  misses per 64-entry chunk of the top-k row, then prefix
+    int* totals;    // [2]   hits, misses
+    uint8_t* hit;   // [B]   slot was hit this step
+};
+
+__host__ __device__ inline size_t swap_in_lds_bytes_impl(int B, int K, int hash_bits)
+{
+    const size_t ints = (size_t(1) << hash_bits) + 4 * size_t(K) + (B + 63) / 64 + (K + 63) / 64 + 4;
+    return ints * 4 + ((size_t(B) + 3) & ~size_t(3));
+}
+
+__device__ inline SwapInLds carve_lds(int* smem, int B, int K, int hash_bits)
+{
+    SwapInLds s;
+    s.hash = smem;
+    s.topk_s = s.hash + (1 << hash_bits);
+    s.out_s = s.topk_s + K;
+    s.plan_t = s.out_s + K;
+    s.plan_v = s.plan_t + K;
+    s.cnt_b = s.plan_v + K;
+    s.cnt_k = s.cnt_b + (B + 63) / 64;
+    s.totals = s.cnt_k + (K + 63) / 64;
+    s.hit = reinterpret_cast<uint8_t*>(s.totals + 4);
+    return s;
+}
+
+// A batch row whose device-side preconditions fail resolves to -1 and changes
+// nothing else; every thread passes the flags it saw.
+__device__ void fail_row(const SwapInArgs& a, int b, uint32_t flags)
+{
+    for (int i = threadIdx.x; i < a.K; i += blockDim.x) a.out[size_t(b) * a.K + i] = -1;
+    if (flags) atomicOr(a.err, flags);
+    if (threadIdx.x == 0) a.plan_count[b] = 0;
+}
+
+// EB / EK: 64-entry chunks of the LRU list / top-k row held per wave.
+template <int EB, int EK>
+__global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
+{
+    extern __shared__ int smem[];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nthr / kWave;
+    const int B = a.B, K = a.K;
+    const int32_t* topk = a.topk + size_t(b) * K;
+    int32_t* out = a.out + size_t(b) * K;
+    const int L = a.seq_lens[b];
+
+    // Tier 0 (resident request) and the short-sequence fast path: the slot
+    // is the position; no state, no plan, no copy.
+    if ((a.resident && a.resident[b]) || L <= B) {
+        for (int i = tid; i < K; i += nthr) out[i] = topk[i];
+        if (tid == 0) a.plan_count[b] = 0;
+        return;
+    }
+    const int r = a.req_idx ? a.req_idx[b] : b;
+    if (r < 0 || r >= a.R) { fail_row(a, b, HISPARSE_DERR_REQ_IDX); return; }
+    if (L > a.max_seq) { fail_row(a, b, HISPARSE_DERR_SEQ_LEN); return; }
+
+    SwapInLds s = carve_lds(smem, B, K, a.hash_bits);
+    const int hmask = (1 << a.hash_bits) - 1;
+    const int ncb = (B + 63) / 64, nck = (K + 63) / 64;
+    int32_t* lru = a.lru + size_t(r) * B;
+    int32_t* tok = a.tok + size_t(r) * B;
+
+    // -- classify the top-k row ------------------------------------------
+    for (int h = tid; h < (1 << a.hash_bits); h += nthr) s.hash[h] = -1;
+    for (int x = tid; x < B; x += nthr) s.hit[x] = 0;
+    int t_own[EK];
+    uint32_t err = 0;
+#pragma unroll
+    for (int k = 0; k < EK; ++k) {
+        const int c = k * nwaves + wave, i = c * kWave + lane;
+        int t = -1;
+        if (c < nck && i < K) {
+            t = topk[i];
+            int cls;
+            if (t == -1) cls = -1;
+            else if (t < -1 || t >= L) { cls = -1; err |= HISPARSE_DERR_TOPK_RANGE; }
+            else if (t == L - 1) cls = B;          // newest token: its own row
+            else cls = kMissMark;
+            s.topk_s[i] = t;
+            s.out_s[i] = cls;
+        }
+        t_own[k] = t;
+    }
+    __syncthreads();
+
+    // -- LDS hash of candidate positions: position -> top-k index --------
+#pragma unroll
+    for (int k = 0; k < EK; ++k) {
+        const int c = k * nwaves + wave, i = c * kWave + lane;
+        const int t = t_own[k];
+        if (c < nck && i < K && t >= 0 && t < L - 1) {
+            uint32_t h = hash_slot(t, a.hash_bits);
+            for (;;) {   // the table has at least 2K entries, so an empty one is always reached
+                const int prev = atomicCAS(&s.hash[h], -1, i);
+                if (prev == -1) break;
+                if (s.topk_s[prev] == t) { err |= HISPARSE_DERR_TOPK_DUP; break; }
+                h = (h + 1) & hmask;
+            }
+        }
+    }
+    if (__syncthreads_or(err != 0)) {
+        fail_row(a, b, err);
+        return;
+    }
+
+    // -- hit detection: probe every slot's position ----------------------
+    for (int x = tid; x < B; x += nthr) {
+        const int t = tok[x];
+        if (t >= 0 && t < L - 1) {
+            uint32_t h = hash_slot(t, a.hash_bits);
+            for (;;) {
+                const int i = s.hash[h];
+                if (i < 0) break;
+                if (s.topk_s[i] == t) {
+                    if (atomicCAS(&s.out_s[i], kMissMark, x) == kMissMark) s.hit[x] = 1;
+                    else err |= HISPARSE_DERR_STATE;   // two slots claim one position
+                    break;
+                }
+                h = (h + 1) & hmask;
+            }
+        } else if (t < -1 || t >= a.max_seq) {
+            err |= HISPARSE_DERR_STATE;
+        }
+    }
+    __syncthreads();
+
+    // -- ballots: hits along the LRU list, misses along the top-k row ----
+    int s_own[EB], lp_b[EB];
+    uint32_t hbits = 0;
+#pragma unroll
+    for (int k = 0; k < EB; ++k) {
+        const int c = k * nwaves + wave, j = c * kWave + lane;
+        s_own[k] = 0;
+        lp_b[k] = 0;
+        if (c < ncb) {
+            bool f = false;
+            if (j < B) {
+                int x = lru[j];
+                if (x < 0 || x >= B) { err |= HISPARSE_DERR_STATE; x = 0; }
+                s_own[k] = x;
+                f = s.hit[x] != 0;
+            }
+            const uint64_t m = __ballot(f);
+            lp_b[k] = lanes_below(m);
+            hbits |= uint32_t(f) << k;
+            if (lane == 0) s.cnt_b[c] = __popcll(m);
+        }
+    }
+    int lp_k[EK];
+    uint32_t mbits = 0;
+#pragma unroll
+    for (int k = 0; k < EK; ++k) {
+        const int c = k * nwaves + wave, i = c * kWave + lane;
+        lp_k[k] = 0;
+        if (c < nck) {
+            const bool miss = i < K && s.out_s[i] == kMissMark;
+            const uint64_t m = __ballot(miss);
+            lp_k[k] = lanes_below(m);
+            mbits |= uint32_t(miss) << k;
+            if (lane == 0) s.cnt_k[c] = __popcll(m);
+        }
+    }
+    if (__syncthreads_or(err != 0)) {
+        fail_row(a, b, err);
+        return;
+    }
+
+    // -- chunk prefix sums -------------------------------------------------
+    if (wave == 0) {
+        const int n_hit = wave_exclusive_scan(s.cnt_b, ncb);
+        if (lane == 0) s.totals[0] = n_hit;
+    }
+    if (wave == (nwaves > 1 ? 1 : 0)) {
+        const int n_miss = wave_exclusive_scan(s.cnt_k, nck);
+        if (lane == 0) s.totals[1] = n_miss;
+    }
+    __syncthreads();
+
+    const int n_hit = s.totals[0], M = s.totals[1];
+    const int n_keep = B - n_hit;   // non-hit slots; >= M because K <= B
+    if (n_keep < M) {               // only when the LRU list repeats a slot
+        fail_row(a, b, HISPARSE_DERR_STATE);
+        return;
+    }
+
+    // -- LRU reorder and victim choice ------------------------------------
+    // new order: non-hit slots n >= M, then hit slots, then victims n < M.
+#pragma unroll
+    for (int k = 0; k < EB; ++k) {
+        const int c = k * nwaves + wave, j = c * kWave + lane;
+        if (c < ncb && j < B) {
+            const int hits_before = s.cnt_b[c] + lp_b[k];
+            const int x = s_own[k];
+            int pos;
+            if ((hbits >> k) & 1u) {
+                pos = n_keep - M + hits_before;
+            } else {
+                const int n = j - hits_before;
+                if (n >= M) {
+                    pos = n - M;
+                } else {
+                    pos = B - M + n;
+                    s.plan_v[n] = x;
+                }
+            }
+            lru[pos] = x;
+        }
+    }
+    int m_own[EK];
+#pragma unroll
+    for (int k = 0; k < EK; ++k) {
+        const int c = k * nwaves + wave;
+        m_own[k] = -1;
+        if (c < nck && ((mbits >> k) & 1u)) {
+            const int m = s.cnt_k[c] + lp_k[k];
+            s.plan_t[m] = t_own[k];
+            m_own[k] = m;
+        }
+    }
+    __syncthreads();
+
+    // -- outputs, slot map, plan row ----------------------------------------
+#pragma unroll
+    for (int k = 0; k < EK; ++k) {
+        const int c = k * nwaves + wave, i = c * kWave + lane;
+        if (c < nck && i < K) out[i] = m_own[k] >= 0 ? s.plan_v[m_own[k]] : s.out_s[i];
+    }
+    int32_t* pp = a.plan_pos + size_t(b) * K;
+    int32_t* ps = a.plan_slot + size_t(b) * K;
+    for (int m = tid; m < M; m += nthr) {
+        const int t = s.plan_t[m], v = s.plan_v[m];
+        tok[v] = t;
+        pp[m] = t;
+        ps[m] = v;
+    }
+    if (tid == 0) a.plan_count[b] = M;
+
+    // -- miss copy: pinned host rows -> victim slots -----------------------
+    const uint8_t* src = a.host + size_t(r) * a.max_seq * a.rb;
+    uint8_t* dst = a.hot + size_t(r) * (B + 1) * a.rb;
+    const int* pt = s.plan_t;
+    const int* pv = s.plan_v;
+    copy_rows(src, dst, M, a.rb, tid, nthr,
+              [pt](int m) { return pt[m]; }, [pv](int m) { return pv[m]; });
+}
+
+// ---------------------------------------------------------------------------
+// replay, backup, forward write, admission
+// ---------------------------------------------------------------------------
+struct ReplayArgs {
+    const int32_t* pos;
+    const int32_t* slot;
+    const int32_t* count;
+    const int32_t* req_idx;
+    const uint8_t* host;
+    uint8_t* hot;
+    uint32_t* err;
+    int32_t nb, R, B, K, rb, max_seq;
+};
+
+// Small fixed grid: workgroup w takes batch rows w, w + grid, ...
+__global__ __launch_bounds__(256) void replay_kernel(ReplayArgs a)
+{
+    for (int b = blockIdx.x; b < a.nb; b += gridDim.x) {
+        const int r = a.req_idx ? a.req_idx[b] : b;
+        const int cnt = a.count[b];
+        if (r < 0 || r >= a.R) {
+            if (threadIdx.x == 0) atomicOr(a.err, HISPARSE_DERR_REQ_IDX);
+            continue;
+        }
+        if (cnt <= 0) {
+            if (cnt < 0 && threadIdx.x == 0) atomicOr(a.err, HISPARSE_DERR_PLAN);
+            continue;
+        }
+        if (cnt > a.K) {
+            if (threadIdx.x == 0) atomicOr(a.err, HISPARSE_DERR_PLAN);
+            continue;
+        }
+        const int32_t* pos = a.pos + size_t(b) * a.K;
+        const int32_t* slot = a.slot + size_t(b) * a.K;
+        // every pair must address rows inside the pool and the buffer
+        bool bad = false;
+        for (int m = threadIdx.x; m < cnt; m += blockDim.x) {
+            const int t = pos[m], v = slot[m];
+            if (t < 0 || t >= a.max_seq || v < 0 || v >= a.B) bad = true;
+        }
+        if (__syncthreads_or(bad)) {
+            if (threadIdx.x == 0) atomicOr(a.err, HISPARSE_DERR_PLAN);
+            continue;
+        }
+        copy_rows(a.host + size_t(r) * a.max_seq * a.rb, a.hot + size_t(r) * (a.B + 1) * a.rb,
+                  cnt, a.rb, threadIdx.x, blockDim.x,
+                  [pos](int m) { return pos[m]; }, [slot](int m) { return slot[m]; });
+        __syncthreads();
+    }
+}
+
+struct RowArgs {
+    const int32_t* seq_lens;
+    const uint8_t* resident;
+    const int32_t* req_idx;
+    const uint8_t* src;          // store_newest: new rows [nb][rb]
+    const uint8_t* host_c;       // backup: hot buffer (read)
+    uint8_t* host;               // backup: host pool (written)
+    uint8_t* hot;                // store_newest: hot buffer (written)
+    uint32_t* err;
+    int32_t nb, R, B, rb, max_seq;
+};
+
+__device__ __forceinline__ void copy_one_row(const uint8_t* src, uint8_t* dst, int rb)
+{
+    for (int c = threadIdx.x; c < (rb >> 4); c += blockDim.x) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t(c) << 4));
+        *reinterpret_cast<u32x4*>(dst + (size_t(c) << 4)) = v;
+    }
+}
+
+// One wave per batch row: the forward's new KV row -> newest-token row.
+__global__ __launch_bounds__(64) void store_newest_kernel(RowArgs a)
+{
+    const int b = blockIdx.x;
+    if (a.resident && a.resident[b]) return;
+    const int r = a.req_idx ? a.req_idx[b] : b;
+    const int L = a.seq_lens[b];
+    if (r < 0 || r >= a.R || L < 1) {
+        if (threadIdx.x == 0) atomicOr(a.err, (r < 0 || r >= a.R) ? HISPARSE_DERR_REQ_IDX : HISPARSE_DERR_SEQ_LEN);
+        return;
+    }
+    const int row = L <= a.B ? L - 1 : a.B;
+    copy_one_row(a.src + size_t(b) * a.rb, a.hot + (size_t(r) * (a.B + 1) + row) * a.rb, a.rb);
+}
+
+// One wave per batch row: newest-token row -> host pool position L-1.
+__global__ __launch_bounds__(64) void backup_kernel(RowArgs a)
+{
+    const int b = blockIdx.x;
+    if (a.resident && a.resident[b]) return;
+    const int r = a.req_idx ? a.req_idx[b] : b;
+    const int L = a.seq_lens[b];
+    if (r < 0 || r >= a.R || L < 1 || L > a.max_seq) {
+        if (threadIdx.x == 0) atomicOr(a.err, (r < 0 || r >= a.R) ? HISPARSE_DERR_REQ_IDX : HISPARSE_DERR_SEQ_LEN);
+        return;
+    }
+    const int row = L <= a.B ? L - 1 : a.B;
+    copy_one_row(a.host_c + (size_t(r) * (a.B + 1) + row) * a.rb,
+                 a.host + (size_t(r) * a.max_seq + (L - 1)) * a.rb, a.rb);
+}
+
+__global__ __launch_bounds__(256) void init_state_kernel(int32_t* lru, int32_t* tok, int R, int B)
+{
+    const size_t n = size_t(R) * B;
+    for (size_t e = size_t(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += size_t(gridDim.x) * blockDim.x) {
+        lru[e] = int32_t(e % B);
+        tok[e] = -1;
+    }
+}
+
+__global__ __launch_bounds__(256) void admit_state_kernel(int32_t* lru, int32_t* tok, const int32_t* req_ids,
+                                                          const int32_t* L0s, int R, int B, uint32_t* err)
+{
+    const int r = req_ids[blockIdx.x];
+    const int L0 = L0s[blockIdx.x];
+    if (r < 0 || r >= R || L0 < 0) {
+        if (threadIdx.x == 0) atomicOr(err, (r < 0 || r >= R) ? HISPARSE_DERR_REQ_IDX : HISPARSE_DERR_SEQ_LEN);
+        return;
+    }
+    for (int x = threadIdx.x; x < B; x += blockDim.x) {
+        lru[size_t(r) * B + x] = x;
+        tok[size_t(r) * B + x] = L0 <= B ? x : -1;
+    }
+}
+
+// grid (n, parts): rows [0, L0) of a request, host pool -> hot buffer (same
+// offsets: slot = position), split over `parts` workgroups.
+__global__ __launch_bounds__(256) void admit_fill_kernel(const uint8_t* host, uint8_t* hot, const int32_t* req_ids,
+                                                         const int32_t* L0s, int R, int B, int rb, int max_seq)
+{
+    const int r = req_ids[blockIdx.x];
+    const int L0 = L0s[blockIdx.x];
+    if (r < 0 || r >= R || L0 <= 0 || L0 > B || L0 > max_seq) return;
+    const size_t chunks = size_t(L0) * (rb >> 4);
+    const uint8_t* src = host + size_t(r) * max_seq * rb;
+    uint8_t* dst = hot + size_t(r) * (B + 1) * rb;
+    for (size_t c = size_t(blockIdx.y) * blockDim.x + threadIdx.x; c < chunks; c += size_t(gridDim.y) * blockDim.x) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (c << 4)));
+        *reinterpret_cast<u32x4*>(dst + (c << 4)) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+typedef void (*SwapInFn)(SwapInArgs);
+
+template <int EB, int EK>
+SwapInFn pick2() { return &swap_in_kernel<EB, EK>; }
+
+template <int EB>
+SwapInFn pick_k(int ek)
+{
+    if (ek <= 1) return pick2<EB, 1>();
+    if (ek <= 2) return pick2<EB, 2>();
+    if (ek <= 4) return pick2<EB, 4>();
+    return nullptr;
+}
+
+SwapInFn pick_kernel(int eb, int ek)
+{
+    if (eb <= 1) return pick_k<1>(ek);
+    if (eb <= 2) return pick_k<2>(ek);
+    if (eb <= 4) return pick_k<4>(ek);
+    if (eb <= 8) return pick_k<8>(ek);
+    if (eb <= 16) return pick_k<16>(ek);
+    return nullptr;
+}
+
+int hash_bits_for(int K)
+{
+    int bits = 1;
+    while ((1 << bits) < 2 * K) ++bits;
+    return bits;
+}
+
+}  // namespace
+
+struct hisparse_ctx {
+    int device = 0;
+    int32_t K = 0, B = 0, layers = 0, R = 0, max_seq = 0, rb = 0;
+    int block = kDefaultBlock, replay_grid = kDefaultReplayGrid, hash_bits = 1;
+    size_t lds = 0;
+    SwapInFn swap_in_fn = nullptr;
+    std::vector<const uint8_t*> host;   // device-usable address of each layer's host pool
+    std::vector<uint8_t*> hot;
+    std::vector<int32_t> anchor_of;
+    std::vector<int32_t*> lru, tok;     // per layer; null for skip layers
+    uint32_t* err = nullptr;
+};
+
+namespace {
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? HISPARSE_OK : HISPARSE_EHIP(e); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The host pool must be pinned host memory the GPU can address; returns the
+// device-side address of `p`, or null.
+const uint8_t* device_view_of_host(void* p, size_t bytes)
+{
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) { (void)hipGetLastError(); return nullptr; }
+    if (at.type != hipMemoryTypeHost || at.devicePointer == nullptr) return nullptr;
+    hipPointerAttribute_t at2;
+    void* last = static_cast<uint8_t*>(p) + bytes - 1;
+    if (hipPointerGetAttributes(&at2, last) != hipSuccess) { (void)hipGetLastError(); return nullptr; }
+    if (at2.type != hipMemoryTypeHost || at2.devicePointer == nullptr) return nullptr;
+    if (static_cast<uint8_t*>(at2.devicePointer) - static_cast<uint8_t*>(at.devicePointer) != ptrdiff_t(bytes - 1))
+        return nullptr;
+    return static_cast<const uint8_t*>(at.devicePointer);
+}
+
+bool is_device_memory(void* p, size_t bytes)
+{
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) { (void)hipGetLastError(); return false; }
+    if (at.type != hipMemoryTypeDevice) return false;
+    void* last = static_cast<uint8_t*>(p) + bytes - 1;
+    if (hipPointerGetAttributes(&at, last) != hipSuccess) { (void)hipGetLastError(); return false; }
+    return at.type == hipMemoryTypeDevice;
+}
+
+bool is_anchor(const hisparse_ctx* c, int32_t l)
+{
+    return l >= 0 && l < c->layers && c->anchor_of[l] == l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hisparse_version(void) { return 1; }
+
+size_t hisparse_swap_in_lds_bytes(int32_t top_k, int32_t device_buffer_size)
+{
+    if (top_k <= 0 || device_buffer_size <= 0) return 0;
+    return swap_in_lds_bytes_impl(device_buffer_size, top_k, hash_bits_for(top_k));
+}
+
+const char* hisparse_strerror(int code)
+{
+    if (code == HISPARSE_OK) return "ok";
+    if (code == HISPARSE_EINVAL) return "invalid argument";
+    if (code == HISPARSE_ENOMEM) return "out of memory";
+    if (code <= -1000) return hipGetErrorString(static_cast<hipError_t>(-code - 1000));
+    return "unknown error";
+}
+
+int hisparse_host_alloc(size_t bytes, uint32_t flags, void** out)
+{
+    if (!out || bytes == 0 || (flags & ~3u) || flags == 3u) return HISPARSE_EINVAL;
+    unsigned hf = hipHostMallocMapped | hipHostMallocPortable;
+    if (flags == HISPARSE_HOST_COHERENT) hf |= hipHostMallocCoherent;
+    if (flags == HISPARSE_HOST_NONCOHERENT) hf |= hipHostMallocNonCoherent;
+    void* p = nullptr;
+    hipError_t e = hipHostMalloc(&p, bytes, hf);
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) { (void)hipGetLastError(); return HISPARSE_ENOMEM; }
+    if (e != hipSuccess) { (void)hipGetLastError(); return HISPARSE_EHIP(e); }
+    *out = p;
+    return HISPARSE_OK;
+}
+
+int hisparse_host_free(void* p)
+{
+    if (!p) return HISPARSE_OK;
+    return hip_rc(hipHostFree(p));
+}
+
+int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out)
+{
+    if (!cfg || !out) return HISPARSE_EINVAL;
+    *out = nullptr;
+    const int K = cfg->top_k, B = cfg->device_buffer_size;
+    if (K < 1 || B < 1 || K > B || B > kMaxB || K > kMaxK) return HISPARSE_EINVAL;
+    if (cfg->num_layers < 1 || cfg->max_requests < 1 || cfg->max_seq_len < 1) return HISPARSE_EINVAL;
+    if (cfg->row_bytes < 16 || cfg->row_bytes % 16) return HISPARSE_EINVAL;
+    if (!cfg->host_pool || !cfg->hot_buffer || !cfg->anchor_of) return HISPARSE_EINVAL;
+    int block = cfg->block_size ? cfg->block_size : kDefaultBlock;
+    if (block < 128 || block > 1024 || block % kWave) return HISPARSE_EINVAL;
+    int replay_grid = cfg->replay_grid ? cfg->replay_grid : kDefaultReplayGrid;
+    if (replay_grid < 1 || replay_grid > 65535) return HISPARSE_EINVAL;
+    const size_t host_bytes = size_t(cfg->max_requests) * cfg->max_seq_len * cfg->row_bytes;
+    const size_t hot_bytes = size_t(cfg->max_requests) * (B + 1) * size_t(cfg->row_bytes);
+    if (size_t(cfg->max_requests) * cfg->max_seq_len > size_t(INT32_MAX) * 64) return HISPARSE_EINVAL;
+
+    hisparse_ctx* c = new (std::nothrow) hisparse_ctx;
+    if (!c) return HISPARSE_ENOMEM;
+    c->K = K; c->B = B; c->layers = cfg->num_layers; c->R = cfg->max_requests;
+    c->max_seq = cfg->max_seq_len; c->rb = cfg->row_bytes;
+    c->block = block; c->replay_grid = replay_grid;
+    c->hash_bits = hash_bits_for(K);
+    c->anchor_of.assign(cfg->anchor_of, cfg->anchor_of + cfg->num_layers);
+    auto fail = [&](int rc) { hisparse_destroy(c); return rc; };
+
+    for (int l = 0; l < c->layers; ++l) {
+        const int g = c->anchor_of[l];
+        if (g < 0 || g >= c->layers || c->anchor_of[g] != g) return fail(HISPARSE_EINVAL);
+        void* hp = cfg->host_pool[l];
+        void* dp = cfg->hot_buffer[l];
+        if (!hp || !dp || !aligned16(hp) || !aligned16(dp)) return fail(HISPARSE_EINVAL);
+        const uint8_t* dv = device_view_of_host(hp, host_bytes);
+        if (!dv || !aligned16(dv)) return fail(HISPARSE_EINVAL);
+        if (!is_device_memory(dp, hot_bytes)) return fail(HISPARSE_EINVAL);
+        c->host.push_back(dv);
+        c->hot.push_back(static_cast<uint8_t*>(dp));
+    }
+    if (hipGetDevice(&c->device) != hipSuccess) return fail(HISPARSE_EHIP(hipGetLastError()));
+
+    const int nwaves = block / kWave;
+    const int eb = ((B + 63) / 64 + nwaves - 1) / nwaves;
+    const int ek = ((K + 63) / 64 + nwaves - 1) / nwaves;
+    c->swap_in_fn = pick_kernel(eb, ek);
+    if (!c->swap_in_fn) return fail(HISPARSE_EINVAL);
+    c->lds = swap_in_lds_bytes_impl(B, K, c->hash_bits);
+    int max_lds = 0;
+    if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device) != hipSuccess)
+        return fail(HISPARSE_EHIP(hipGetLastError()));
+    if (c->lds > size_t(max_lds)) return fail(HISPARSE_EINVAL);
+    if (c->lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(c->swap_in_fn),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(c->lds));
+        if (e != hipSuccess) return fail(HISPARSE_EHIP(e));
+    }
+
+    const size_t state_bytes = size_t(c->R) * B * sizeof(int32_t);
+    c->lru.assign(c->layers, nullptr);
+    c->tok.assign(c->layers, nullptr);
+    for (int l = 0; l < c->layers; ++l) {
+        if (!is_anchor(c, l)) continue;   // skip layers share their anchor's state
+        hipError_t e1 = hipMalloc(&c->lru[l], state_bytes);
+        hipError_t e2 = e1 == hipSuccess ? hipMalloc(&c->tok[l], state_bytes) : e1;
+        if (e1 != hipSuccess || e2 != hipSuccess) { (void)hipGetLastError(); return fail(HISPARSE_ENOMEM); }
+        hipLaunchKernelGGL(init_state_kernel, dim3(1024), dim3(256), 0, nullptr, c->lru[l], c->tok[l], c->R, B);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(HISPARSE_EHIP(e));
+    }
+    if (hipMalloc(&c->err, sizeof(uint32_t)) != hipSuccess) { (void)hipGetLastError(); return fail(HISPARSE_ENOMEM); }
+    hipError_t e = hipMemset(c->err, 0, sizeof(uint32_t));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(HISPARSE_EHIP(e));
+    *out = c;
+    return HISPARSE_OK;
+}
+
+void hisparse_destroy(hisparse_ctx* c)
+{
+    if (!c) return;
+    for (int32_t* p : c->lru) if (p) (void)hipFree(p);
+    for (int32_t* p : c->tok) if (p) (void)hipFree(p);
+    if (c->err) (void)hipFree(c->err);
+    delete c;
+}
+
+int hisparse_admit(hisparse_ctx* c, int32_t anchor_layer, const int32_t* req_ids, const int32_t* seq_len0,
+                   int32_t n, hipStream_t stream)
+{
+    if (!c || !is_anchor(c, anchor_layer) || n < 0 || n > c->R) return HISPARSE_EINVAL;
+    if (n == 0) return HISPARSE_OK;
+    if (!req_ids || !seq_len0) return HISPARSE_EINVAL;
+    hipLaunchKernelGGL(admit_state_kernel, dim3(n), dim3(256), 0, stream, c->lru[anchor_layer],
+                       c->tok[anchor_layer], req_ids, seq_len0, c->R, c->B, c->err);
+    for (int l = 0; l < c->layers; ++l) {
+        if (c->anchor_of[l] != anchor_layer) continue;
+        hipLaunchKernelGGL(admit_fill_kernel, dim3(n, 64), dim3(256), 0, stream, c->host[l], c->hot[l],
+                           req_ids, seq_len0, c->R, c->B, c->rb, c->max_seq);
+    }
+    return hip_rc(hipGetLastError());
+}
+
+int hisparse_store_newest(hisparse_ctx* c, int32_t layer, const void* new_rows, const int32_t* seq_lens,
+                          const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb, hipStream_t stream)
+{
+    if (!c || layer < 0 || layer >= c->layers || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
+    if (nb == 0) return HISPARSE_OK;
+    if (!new_rows || !seq_lens || !aligned16(new_rows)) return HISPARSE_EINVAL;
+    RowArgs a{};
+    a.seq_lens = seq_lens; a.resident = resident_mask; a.req_idx = req_idx;
+    a.src = static_cast<const uint8_t*>(new_rows); a.hot = c->hot[layer]; a.err = c->err;
+    a.nb = nb; a.R = c->R; a.B = c->B; a.rb = c->rb; a.max_seq = c->max_seq;
+    hipLaunchKernelGGL(store_newest_kernel, dim3(nb), dim3(64), 0, stream, a);
+    return hip_rc(hipGetLastError());
+}
+
+int hisparse_swap_in(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_idx, const int32_t* seq_lens,
+                     const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb, int32_t* out_slots,
+                     hisparse_plan plan_row, hipStream_t stream)
+{
+    if (!c || !is_anchor(c, anchor_layer) || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
+    if (nb == 0) return HISPARSE_OK;
+    if (!topk_idx || !seq_lens || !out_slots || !plan_row.pos || !plan_row.slot || !plan_row.count)
+        return HISPARSE_EINVAL;
+    SwapInArgs a{};
+    a.topk = topk_idx; a.seq_lens = seq_lens; a.resident = resident_mask; a.req_idx = req_idx;
+    a.out = out_slots; a.plan_pos = plan_row.pos; a.plan_slot = plan_row.slot; a.plan_count = plan_row.count;
+    a.lru = c->lru[anchor_layer]; a.tok = c->tok[anchor_layer];
+    a.host = c->host[anchor_layer]; a.hot = c->hot[anchor_layer]; a.err = c->err;
+    a.R = c->R; a.B = c->B; a.K = c->K; a.rb = c->rb; a.max_seq = c->max_seq; a.hash_bits = c->hash_bits;
+    void* args[] = {&a};
+    return hip_rc(hipLaunchKernel(reinterpret_cast<const void*>(c->swap_in_fn), dim3(nb), dim3(c->block), args,
+                                  c->lds, stream));
+}
+
+int hisparse_replay_plan(hisparse_ctx* c, int32_t skip_layer, hisparse_plan plan_row, const int32_t* req_idx,
+                         int32_t nb, hipStream_t side_stream)
+{
+    if (!c || skip_layer < 0 || skip_layer >= c->layers || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
+    if (nb == 0) return HISPARSE_OK;
+    if (!plan_row.pos || !plan_row.slot || !plan_row.count) return HISPARSE_EINVAL;
+    ReplayArgs a{};
+    a.pos = plan_row.pos; a.slot = plan_row.slot; a.count = plan_row.count; a.req_idx = req_idx;
+    a.host = c->host[skip_layer]; a.hot = c->hot[skip_layer]; a.err = c->err;
+    a.nb = nb; a.R = c->R; a.B = c->B; a.K = c->K; a.rb = c->rb; a.max_seq = c->max_seq;
+    const int grid = nb < c->replay_grid ? nb : c->replay_grid;
+    hipLaunchKernelGGL(replay_kernel, dim3(grid), dim3(256), 0, side_stream, a);
+    return hip_rc(hipGetLastError());
+}
+
+int hisparse_backup(hisparse_ctx* c, int32_t layer, const int32_t* seq_lens, const uint8_t* resident_mask,
+                    const int32_t* req_idx, int32_t nb, hipStream_t stream)
+{
+    if (!c || layer < 0 || layer >= c->layers || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
+    if (nb == 0) return HISPARSE_OK;
+    if (!seq_lens) return HISPARSE_EINVAL;
+    RowArgs a{};
+    a.seq_lens = seq_lens; a.resident = resident_mask; a.req_idx = req_idx;
+    a.host_c = c->hot[layer]; a.host = const_cast<uint8_t*>(c->host[layer]); a.err = c->err;
+    a.nb = nb; a.R = c->R; a.B = c->B; a.rb = c->rb; a.max_seq = c->max_seq;
+    hipLaunchKernelGGL(backup_kernel, dim3(nb), dim3(64), 0, stream, a);
+    return hip_rc(hipGetLastError());
+}
+
+int hisparse_get_state(hisparse_ctx* c, int32_t anchor_layer, int32_t* lru, int32_t* slot_tok, hipStream_t stream)
+{
+    if (!c || !is_anchor(c, anchor_layer) || !lru || !slot_tok) return HISPARSE_EINVAL;
+    const size_t bytes = size_t(c->R) * c->B * sizeof(int32_t);
+    hipError_t e = hipMemcpyAsync(lru, c->lru[anchor_layer], bytes, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(slot_tok, c->tok[anchor_layer], bytes, hipMemcpyDeviceToDevice, stream);
+    return hip_rc(e);
+}
+
+int hisparse_set_state(hisparse_ctx* c, int32_t anchor_layer, const int32_t* lru, const int32_t* slot_tok,
+                       hipStream_t stream)
+{
+    if (!c || !is_anchor(c, anchor_layer) || !lru || !slot_tok) return HISPARSE_EINVAL;
+    const size_t bytes = size_t(c->R) * c->B * sizeof(int32_t);
+    hipError_t e = hipMemcpyAsync(c->lru[anchor_layer], lru, bytes, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(c->tok[anchor_layer], slot_tok, bytes, hipMemcpyDeviceToDevice, stream);
+    return hip_rc(e);
+}
+
+int hisparse_get_error(hisparse_ctx* c, uint32_t* flags, int clear, hipStream_t stream)
+{
+    if (!c || !flags) return HISPARSE_EINVAL;
+    hipError_t e = hipMemcpyAsync(flags, c->err, sizeof(uint32_t), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess && clear) e = hipMemsetAsync(c->err, 0, sizeof(uint32_t), stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    return hip_rc(e);
+}
+
+}  // extern "C"

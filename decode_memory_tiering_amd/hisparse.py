@@ -1,0 +1,321 @@
+"""Python binding of ``libhisparse.so`` (the C ABI declared in include/hisparse.h).
+
+Argument marshalling only: every step of the swap-in path runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and streams.  The
+library must be built (``python -m decode_memory_tiering_amd.build``); if it
+is missing, loading fails loudly -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhisparse.so")
+
+HISPARSE_OK = 0
+HISPARSE_EINVAL = -22
+HISPARSE_ENOMEM = -12
+
+HISPARSE_DERR_TOPK_RANGE = 0x1
+HISPARSE_DERR_TOPK_DUP = 0x2
+HISPARSE_DERR_SEQ_LEN = 0x4
+HISPARSE_DERR_REQ_IDX = 0x8
+HISPARSE_DERR_STATE = 0x10
+HISPARSE_DERR_PLAN = 0x20
+
+HISPARSE_HOST_DEFAULT = 0
+HISPARSE_HOST_COHERENT = 1
+HISPARSE_HOST_NONCOHERENT = 2
+
+# every entry point include/hisparse.h declares
+EXPORTS = (
+    "hisparse_init", "hisparse_destroy", "hisparse_admit", "hisparse_store_newest",
+    "hisparse_swap_in", "hisparse_replay_plan", "hisparse_backup", "hisparse_get_state",
+    "hisparse_set_state", "hisparse_get_error", "hisparse_host_alloc", "hisparse_host_free",
+    "hisparse_swap_in_lds_bytes", "hisparse_strerror", "hisparse_version",
+)
+
+
+class HisparseError(RuntimeError):
+    def __init__(self, rc: int, what: str):
+        self.rc = rc
+        msg = _lib().hisparse_strerror(rc).decode() if _LIB is not None else str(rc)
+        super().__init__(f"{what} failed: {rc} ({msg})")
+
+
+class hisparse_config(ctypes.Structure):
+    _fields_ = [
+        ("top_k", ctypes.c_int32),
+        ("device_buffer_size", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32),
+        ("max_requests", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("row_bytes", ctypes.c_int32),
+        ("host_pool", ctypes.POINTER(ctypes.c_void_p)),
+        ("hot_buffer", ctypes.POINTER(ctypes.c_void_p)),
+        ("anchor_of", ctypes.POINTER(ctypes.c_int32)),
+        ("block_size", ctypes.c_int32),
+        ("replay_grid", ctypes.c_int32),
+    ]
+
+
+class hisparse_plan(ctypes.Structure):
+    _fields_ = [("pos", ctypes.c_void_p), ("slot", ctypes.c_void_p), ("count", ctypes.c_void_p)]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        _LIB = load_library()
+    return _LIB
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m decode_memory_tiering_amd.build` "
+                           "(the HiSparse path has no fallback)")
+    lib = ctypes.CDLL(path)
+    P, I32, U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32
+    lib.hisparse_init.argtypes = [ctypes.POINTER(hisparse_config), ctypes.POINTER(ctypes.c_void_p)]
+    lib.hisparse_destroy.argtypes = [P]
+    lib.hisparse_destroy.restype = None
+    lib.hisparse_admit.argtypes = [P, I32, P, P, I32, P]
+    lib.hisparse_store_newest.argtypes = [P, I32, P, P, P, P, I32, P]
+    lib.hisparse_swap_in.argtypes = [P, I32, P, P, P, P, I32, P, hisparse_plan, P]
+    lib.hisparse_replay_plan.argtypes = [P, I32, hisparse_plan, P, I32, P]
+    lib.hisparse_backup.argtypes = [P, I32, P, P, P, I32, P]
+    lib.hisparse_get_state.argtypes = [P, I32, P, P, P]
+    lib.hisparse_set_state.argtypes = [P, I32, P, P, P]
+    lib.hisparse_get_error.argtypes = [P, ctypes.POINTER(U32), ctypes.c_int, P]
+    lib.hisparse_host_alloc.argtypes = [ctypes.c_size_t, U32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.hisparse_host_free.argtypes = [P]
+    lib.hisparse_swap_in_lds_bytes.argtypes = [I32, I32]
+    lib.hisparse_swap_in_lds_bytes.restype = ctypes.c_size_t
+    lib.hisparse_strerror.argtypes = [ctypes.c_int]
+    lib.hisparse_strerror.restype = ctypes.c_char_p
+    lib.hisparse_version.argtypes = []
+    for name in EXPORTS:
+        fn = getattr(lib, name)
+        if name not in ("hisparse_destroy", "hisparse_strerror", "hisparse_swap_in_lds_bytes"):
+            fn.restype = ctypes.c_int
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != HISPARSE_OK:
+        raise HisparseError(rc, what)
+
+
+def _ptr(t) -> Optional[int]:
+    """Device (or host) address of a tensor, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    assert t.is_contiguous(), "HiSparse buffers must be contiguous"
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+@dataclass
+class Plan:
+    """One plan row on the device: pos / slot [nb][K], count [nb] (int32)."""
+    pos: "torch.Tensor"
+    slot: "torch.Tensor"
+    count: "torch.Tensor"
+
+    @classmethod
+    def empty(cls, nb: int, K: int, device="cuda") -> "Plan":
+        import torch
+        return cls(torch.zeros(nb, K, dtype=torch.int32, device=device),
+                   torch.zeros(nb, K, dtype=torch.int32, device=device),
+                   torch.zeros(nb, dtype=torch.int32, device=device))
+
+    def c(self) -> hisparse_plan:
+        return hisparse_plan(_ptr(self.pos), _ptr(self.slot), _ptr(self.count))
+
+
+# ---------------------------------------------------------------------------
+# the C ABI, name for name
+# ---------------------------------------------------------------------------
+def hisparse_host_alloc(nbytes: int, flags: int = HISPARSE_HOST_DEFAULT) -> int:
+    p = ctypes.c_void_p()
+    _check(_lib().hisparse_host_alloc(nbytes, flags, ctypes.byref(p)), "hisparse_host_alloc")
+    return int(p.value)
+
+
+def hisparse_host_free(ptr: int) -> None:
+    _check(_lib().hisparse_host_free(ptr), "hisparse_host_free")
+
+
+def hisparse_init(*, top_k: int, device_buffer_size: int, num_layers: int, max_requests: int,
+                  max_seq_len: int, row_bytes: int, host_pool: Sequence[int], hot_buffer: Sequence,
+                  anchor_of: Sequence[int], block_size: int = 0, replay_grid: int = 0) -> int:
+    hp = (ctypes.c_void_p * len(host_pool))(*[int(p) for p in host_pool])
+    hb = (ctypes.c_void_p * len(hot_buffer))(*[_ptr(t) for t in hot_buffer])
+    an = (ctypes.c_int32 * len(anchor_of))(*[int(a) for a in anchor_of])
+    cfg = hisparse_config(top_k, device_buffer_size, num_layers, max_requests, max_seq_len, row_bytes,
+                          ctypes.cast(hp, ctypes.POINTER(ctypes.c_void_p)),
+                          ctypes.cast(hb, ctypes.POINTER(ctypes.c_void_p)),
+                          ctypes.cast(an, ctypes.POINTER(ctypes.c_int32)), block_size, replay_grid)
+    ctx = ctypes.c_void_p()
+    _check(_lib().hisparse_init(ctypes.byref(cfg), ctypes.byref(ctx)), "hisparse_init")
+    return int(ctx.value)
+
+
+def hisparse_destroy(ctx: int) -> None:
+    _lib().hisparse_destroy(ctx)
+
+
+def hisparse_admit(ctx: int, anchor_layer: int, req_ids, seq_len0, stream=None) -> None:
+    _check(_lib().hisparse_admit(ctx, anchor_layer, _ptr(req_ids), _ptr(seq_len0), int(req_ids.shape[0]),
+                                 _stream(stream)), "hisparse_admit")
+
+
+def hisparse_store_newest(ctx: int, layer: int, new_rows, seq_lens, resident_mask=None, req_idx=None,
+                          stream=None) -> None:
+    _check(_lib().hisparse_store_newest(ctx, layer, _ptr(new_rows), _ptr(seq_lens), _ptr(resident_mask),
+                                        _ptr(req_idx), int(seq_lens.shape[0]), _stream(stream)),
+           "hisparse_store_newest")
+
+
+def hisparse_swap_in(ctx: int, anchor_layer: int, topk_idx, seq_lens, resident_mask, req_idx, out_slots,
+                     plan: Plan, stream=None) -> None:
+    _check(_lib().hisparse_swap_in(ctx, anchor_layer, _ptr(topk_idx), _ptr(seq_lens), _ptr(resident_mask),
+                                   _ptr(req_idx), int(topk_idx.shape[0]), _ptr(out_slots), plan.c(),
+                                   _stream(stream)), "hisparse_swap_in")
+
+
+def hisparse_replay_plan(ctx: int, skip_layer: int, plan: Plan, req_idx=None, stream=None) -> None:
+    _check(_lib().hisparse_replay_plan(ctx, skip_layer, plan.c(), _ptr(req_idx), int(plan.count.shape[0]),
+                                       _stream(stream)), "hisparse_replay_plan")
+
+
+def hisparse_backup(ctx: int, layer: int, seq_lens, resident_mask=None, req_idx=None, stream=None) -> None:
+    _check(_lib().hisparse_backup(ctx, layer, _ptr(seq_lens), _ptr(resident_mask), _ptr(req_idx),
+                                  int(seq_lens.shape[0]), _stream(stream)), "hisparse_backup")
+
+
+def hisparse_get_state(ctx: int, anchor_layer: int, lru, slot_tok, stream=None) -> None:
+    _check(_lib().hisparse_get_state(ctx, anchor_layer, _ptr(lru), _ptr(slot_tok), _stream(stream)),
+           "hisparse_get_state")
+
+
+def hisparse_set_state(ctx: int, anchor_layer: int, lru, slot_tok, stream=None) -> None:
+    _check(_lib().hisparse_set_state(ctx, anchor_layer, _ptr(lru), _ptr(slot_tok), _stream(stream)),
+           "hisparse_set_state")
+
+
+def hisparse_get_error(ctx: int, clear: bool = True, stream=None) -> int:
+    v = ctypes.c_uint32()
+    _check(_lib().hisparse_get_error(ctx, ctypes.byref(v), int(clear), _stream(stream)), "hisparse_get_error")
+    return int(v.value)
+
+
+def hisparse_swap_in_lds_bytes(top_k: int, device_buffer_size: int) -> int:
+    return int(_lib().hisparse_swap_in_lds_bytes(top_k, device_buffer_size))
+
+
+def hisparse_strerror(code: int) -> str:
+    return _lib().hisparse_strerror(code).decode()
+
+
+def hisparse_version() -> int:
+    return int(_lib().hisparse_version())
+
+
+# ---------------------------------------------------------------------------
+# a cache object: pinned host pools + device hot buffers + a context
+# ---------------------------------------------------------------------------
+def host_array(ptr: int, shape) -> np.ndarray:
+    """numpy view of pinned host memory (no copy)."""
+    n = int(np.prod(shape))
+    buf = (ctypes.c_uint8 * n).from_address(ptr)
+    return np.ctypeslib.as_array(buf).reshape(shape)
+
+
+class HiSparseCache:
+    """One HiSparse cache: per-layer pinned host pools [R][max_seq][rb] (owned,
+    allocated with hisparse_host_alloc), per-layer device hot buffers
+    [R][B+1][rb] (torch), and the library context."""
+
+    def __init__(self, *, num_layers: int, anchor_of: Sequence[int], R: int, B: int, K: int, rb: int,
+                 max_seq: int, device="cuda", host_flags: int = HISPARSE_HOST_DEFAULT,
+                 block_size: int = 0, replay_grid: int = 0):
+        import torch
+        self.num_layers, self.R, self.B, self.K, self.rb, self.max_seq = num_layers, R, B, K, rb, max_seq
+        self.anchor_of = [int(a) for a in anchor_of]
+        self.device = torch.device(device)
+        self._host_ptrs: List[int] = []
+        self.ctx = 0
+        nbytes = R * max_seq * rb
+        for _ in range(num_layers):
+            self._host_ptrs.append(hisparse_host_alloc(nbytes, host_flags))
+        self.host_np = [host_array(p, (R, max_seq, rb)) for p in self._host_ptrs]
+        self.host = [torch.from_numpy(a) for a in self.host_np]          # CPU views, same memory
+        self.hot = [torch.zeros(R, B + 1, rb, dtype=torch.uint8, device=self.device)
+                    for _ in range(num_layers)]
+        self.ctx = hisparse_init(top_k=K, device_buffer_size=B, num_layers=num_layers, max_requests=R,
+                                 max_seq_len=max_seq, row_bytes=rb, host_pool=self._host_ptrs,
+                                 hot_buffer=self.hot, anchor_of=self.anchor_of, block_size=block_size,
+                                 replay_grid=replay_grid)
+
+    def close(self):
+        if self.ctx:
+            hisparse_destroy(self.ctx)
+            self.ctx = 0
+        self.host, self.host_np = [], []
+        for p in self._host_ptrs:
+            hisparse_host_free(p)
+        self._host_ptrs = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # thin forwards
+    def admit(self, anchor, req_ids, seq_len0, stream=None):
+        hisparse_admit(self.ctx, anchor, req_ids, seq_len0, stream)
+
+    def store_newest(self, layer, new_rows, seq_lens, resident_mask=None, req_idx=None, stream=None):
+        hisparse_store_newest(self.ctx, layer, new_rows, seq_lens, resident_mask, req_idx, stream)
+
+    def swap_in(self, anchor, topk_idx, seq_lens, resident_mask, req_idx, out_slots, plan, stream=None):
+        hisparse_swap_in(self.ctx, anchor, topk_idx, seq_lens, resident_mask, req_idx, out_slots, plan, stream)
+
+    def replay_plan(self, skip_layer, plan, req_idx=None, stream=None):
+        hisparse_replay_plan(self.ctx, skip_layer, plan, req_idx, stream)
+
+    def backup(self, layer, seq_lens, resident_mask=None, req_idx=None, stream=None):
+        hisparse_backup(self.ctx, layer, seq_lens, resident_mask, req_idx, stream)
+
+    def get_state(self, anchor, stream=None):
+        import torch
+        lru = torch.empty(self.R, self.B, dtype=torch.int32, device=self.device)
+        tok = torch.empty_like(lru)
+        hisparse_get_state(self.ctx, anchor, lru, tok, stream)
+        return lru, tok
+
+    def set_state(self, anchor, lru, tok, stream=None):
+        hisparse_set_state(self.ctx, anchor, lru, tok, stream)
+
+    def get_error(self, clear=True, stream=None) -> int:
+        return hisparse_get_error(self.ctx, clear, stream)

@@ -1,0 +1,132 @@
+"""Drive a decode workload through the HIP path (tests and benchmark).
+
+One decode step, for every layer in order (SGLang guide "HiSparse:
+Hierarchical Sparse Attention", "Decode Workflow" and "Shared-index
+prefetch"; vLLM design note "HiSparse local KV offload architecture",
+"Resident device pages" for the verify rows):
+
+  store_newest(l)                        the forward's KV write
+  anchor layer:  swap_in(l), once per verify row s, each with its own plan row
+                 then, with prefetch on, the replays of its skip layers are
+                 issued on the side stream after an event
+  skip layer:    wait for its replay (prefetch) or replay inline
+  backup(l)                              eager backup of the newest token
+
+Every launch goes through the C ABI; this module only allocates tensors,
+moves seeded inputs to the device and orders streams.
+"""
+from __future__ import annotations
+
+import os
+from typing import Dict, List, Optional
+
+import numpy as np
+
+from . import workload as W
+from .hisparse import HISPARSE_HOST_DEFAULT, HiSparseCache, Plan
+
+
+def prefetch_enabled() -> bool:
+    """Skip-layer replays run on a side stream unless HISPARSE_DISABLE_PREFETCH=1
+    (A/B switch; the SGLang guide's "Shared-index prefetch" has the same one)."""
+    return os.environ.get("HISPARSE_DISABLE_PREFETCH", "0") != "1"
+
+
+class GpuRun:
+    def __init__(self, wl: W.Workload, steps: Optional[int] = None, device: str = "cuda",
+                 block_size: int = 0, replay_grid: int = 0, host_flags: int = HISPARSE_HOST_DEFAULT,
+                 prefetch: Optional[bool] = None, fill: bool = True):
+        import torch
+        self.torch = torch
+        self.wl = wl
+        self.steps = wl.steps if steps is None else steps
+        self.dev = torch.device(device)
+        self.max_seq = W.max_seq(wl, self.steps)
+        self.L0 = W.prompt_lens(wl)
+        self.cache = HiSparseCache(num_layers=wl.num_layers, anchor_of=wl.anchor_of, R=wl.R, B=wl.B,
+                                   K=wl.K, rb=wl.rb, max_seq=self.max_seq, device=device,
+                                   host_flags=host_flags, block_size=block_size,
+                                   replay_grid=replay_grid)
+        self.prefetch = prefetch_enabled() if prefetch is None else prefetch
+        res = W.resident_mask(wl)
+        self.resident = torch.from_numpy(res).to(self.dev) if res.any() else None
+        self.resident_np = res
+        self.out = {g: torch.zeros(wl.spec, wl.R, wl.K, dtype=torch.int32, device=self.dev)
+                    for g in wl.anchors}
+        self.plans = {g: [Plan.empty(wl.R, wl.K, self.dev) for _ in range(wl.spec)] for g in wl.anchors}
+        self.side = torch.cuda.Stream(device=self.dev)
+        self.events: Dict[int, "torch.cuda.Event"] = {}
+        if fill:
+            self.fill_and_admit()
+
+    # -- set-up ----------------------------------------------------------------
+    def fill_and_admit(self):
+        torch, wl = self.torch, self.wl
+        for l in range(wl.num_layers):
+            W.fill_host_pool(self.cache.host[l], wl, l, self.L0, self.dev)
+        req = torch.arange(wl.R, dtype=torch.int32, device=self.dev)
+        L0 = torch.from_numpy(self.L0.astype(np.int32)).to(self.dev)
+        for g in wl.anchors:
+            self.cache.admit(g, req, L0)
+        torch.cuda.synchronize(self.dev)
+
+    def seq_lens(self, step: int):
+        return self.torch.from_numpy(W.seq_lens_at(self.wl, step).astype(np.int32)).to(self.dev)
+
+    # -- one decode step ------------------------------------------------------
+    def step(self, topk: Dict[int, "torch.Tensor"], new_kv: "torch.Tensor", seq_lens,
+             between_layers=None, after_swap_in=None):
+        """topk[g]: [S][R][K] int32 (device) for every anchor g; new_kv:
+        [layers][R][rb] uint8 (device); seq_lens: [R] int32 (device).
+        between_layers(l) runs on the main stream after layer l (a stand-in for
+        the layer's other compute); after_swap_in(g, s) runs right after each
+        swap-in (the consumer of that verify row)."""
+        torch, wl, c = self.torch, self.wl, self.cache
+        main = torch.cuda.current_stream(self.dev)
+        for l in range(wl.num_layers):
+            g = wl.anchor_of[l]
+            c.store_newest(l, new_kv[l], seq_lens, self.resident)
+            if g == l:
+                for s in range(wl.spec):
+                    c.swap_in(l, topk[l][s], seq_lens, self.resident, None, self.out[l][s], self.plans[l][s])
+                    if after_swap_in is not None:
+                        after_swap_in(l, s)
+                skips = [x for x in wl.skip_layers if wl.anchor_of[x] == l]
+                if skips and self.prefetch:
+                    ev = torch.cuda.Event()
+                    ev.record(main)
+                    self.side.wait_event(ev)
+                    with torch.cuda.stream(self.side):
+                        for x in skips:
+                            for s in range(wl.spec):
+                                c.replay_plan(x, self.plans[l][s], None, self.side)
+                            e2 = torch.cuda.Event()
+                            e2.record(self.side)
+                            self.events[x] = e2
+            else:
+                if self.prefetch:
+                    main.wait_event(self.events.pop(l))
+                else:
+                    for s in range(wl.spec):
+                        c.replay_plan(l, self.plans[g][s], None, main)
+            c.backup(l, seq_lens, self.resident)
+            if between_layers is not None:
+                between_layers(l)
+
+    def close(self):
+        self.cache.close()
+
+
+def valid_entries(topk_np: np.ndarray) -> int:
+    return int(np.count_nonzero(topk_np >= 0))
+
+
+def new_kv_all_layers(wl: W.Workload, step: int, device) -> "torch.Tensor":
+    import torch
+    return torch.stack([W.new_kv_rows(wl, step, l, device) for l in range(wl.num_layers)])
+
+
+def draw_topk(wl: W.Workload, streams: Dict[int, W.TopkStream], step: int) -> Dict[int, np.ndarray]:
+    """Top-k rows of one decode step for every anchor: [S][R][K] int32."""
+    L = W.seq_lens_at(wl, step)
+    return {g: np.stack([streams[g].rows(step, L, s) for s in range(wl.spec)]) for g in wl.anchors}

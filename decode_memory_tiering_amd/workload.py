@@ -38,7 +38,7 @@ class Workload:
     spec: int = 1                    # verify rows per decode step (speculative decoding)
     n_resident: int = 0              # requests whose KV is fully resident
     topk_kind: str = "mixture"       # "mixture" | "uniform"
-    seq_first: Tuple = ("fixed", 8192)   # ("fixed", L) or ("uniform", lo, hi): L at step 0
+    seq_first: Tuple = ("fixed", 8192)   # ("fixed", L) | ("uniform", lo, hi) | ("list", L_0, ..., L_R-1): L at step 0
     row_format: str = "bf16"         # "bf16" (576 x bf16) | "fp8_656"
     seed: int = 1
 
@@ -86,6 +86,10 @@ def first_seq_lens(wl: Workload) -> np.ndarray:
     if kind == "uniform":
         lo, hi = int(wl.seq_first[1]), int(wl.seq_first[2])
         return _rng(wl.seed, 7001).integers(lo, hi + 1, size=wl.R).astype(np.int32)
+    if kind == "list":
+        vals = np.asarray(wl.seq_first[1:], dtype=np.int32)
+        assert vals.size == wl.R
+        return vals
     raise ValueError(kind)
 
 

@@ -1,0 +1,210 @@
+/*
+ * hisparse.h -- C ABI of the HiSparse decode-step swap-in resolver for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources):
+ *   [SGL]  SGLang guide "HiSparse: Hierarchical Sparse Attention":
+ *          "Decode Workflow" (fast path, hit detection -> LRU reorder -> miss
+ *          copy host to device, eager backup), "HiSparse Config Parameters"
+ *          (top_k, device_buffer_size), "Shared-index prefetch" (the anchor's
+ *          miss plan replayed by a copy-only kernel on a side stream).
+ *   [vLLM] vLLM design note "HiSparse local KV offload architecture":
+ *          "Resident device pages" (one fused resolver: resident page, then
+ *          hot row, then pinned host memory; resident hits exit first; the
+ *          graph-stable request mapping; speculative verify rows),
+ *          "Hot lookup and LRU", "Performance invariants" (no device readback,
+ *          no extra kernel launch, graph-capturable).
+ *
+ * Terms and layouts (all sizes in elements unless stated):
+ *   K   top_k              B   device_buffer_size (token slots per request)
+ *   R   max_requests       rb  row_bytes (one token's KV row, multiple of 16)
+ *   host pool of a layer   [R][max_seq_len][rb] bytes, pinned host memory that
+ *                          the GPU can address (see hisparse_host_alloc)
+ *   hot buffer of a layer  [R][B+1][rb] bytes, device memory.  Rows 0..B-1 are
+ *                          the LRU-managed slots; row B holds the newest token
+ *                          while the sequence is longer than B.
+ *   batch row b            serves request r = req_idx[b] (r = b if req_idx is
+ *                          NULL): the graph-stable mapping taken from the
+ *                          caller's attention metadata.
+ *   seq_lens[b]  L         tokens with KV, the newest (position L-1) included.
+ *   top-k entries          positions in [0, L), distinct, or -1 (padding).
+ *
+ * Output slot ids (out_slots[b][i]):
+ *   resident request       the position itself (the caller's resident block
+ *                          table maps it; resident requests touch no state);
+ *   L <= B (fast path)     the position itself (slot = position);
+ *   otherwise              a row of hot[r]: the slot holding that position, or
+ *                          B for the newest position L-1; -1 for padding.
+ *
+ * Every pointer argument of the hot calls (store_newest, swap_in,
+ * replay_plan, backup) is device memory unless stated; all four are
+ * asynchronous on the given stream, allocate nothing, never read device data
+ * back to the host, and may be captured in a HIP graph.  Ownership: the caller
+ * owns host pools, hot buffers, inputs, outputs and plan buffers; the library
+ * owns only the per-anchor-layer LRU state ([R][B] int32 lru and slot map)
+ * and one device error word.
+ *
+ * Errors: a call returns 0, or a negative code: HISPARSE_EINVAL (bad argument
+ * seen on the host), HISPARSE_ENOMEM, or HISPARSE_EHIP(e) = -(1000 + e) for a
+ * HIP runtime error e.  Host-side checks never read device data.  Broken
+ * device-side preconditions (a top-k entry out of range or repeated, L beyond
+ * the host pool, a request index out of range, corrupt state, a plan entry
+ * out of range) never fault: the affected batch row resolves to all -1 with
+ * a plan count of 0, leaves state and buffers untouched, and sets a bit in
+ * the device error word (hisparse_get_error).  The fast path and the resident
+ * tier address no memory with top-k entries and do not check them.
+ */
+#ifndef HISPARSE_H
+#define HISPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HISPARSE_OK 0
+#define HISPARSE_EINVAL (-22)
+#define HISPARSE_ENOMEM (-12)
+#define HISPARSE_EHIP(e) (-(1000 + (int)(e)))
+
+/* Device error word bits (hisparse_get_error). */
+#define HISPARSE_DERR_TOPK_RANGE 0x1u  /* entry < -1 or >= L */
+#define HISPARSE_DERR_TOPK_DUP   0x2u  /* repeated position in a top-k row */
+#define HISPARSE_DERR_SEQ_LEN    0x4u  /* L < 1, or L > max_seq_len where the host pool is addressed */
+#define HISPARSE_DERR_REQ_IDX    0x8u  /* req_idx[b] outside [0, R) */
+#define HISPARSE_DERR_STATE      0x10u /* lru not a permutation / slot map not injective or out of range */
+#define HISPARSE_DERR_PLAN       0x20u /* replay: count > K, or a (pos, slot) pair out of range */
+
+/* hisparse_host_alloc flags */
+#define HISPARSE_HOST_DEFAULT     0u   /* HIP's default pinned, mapped allocation */
+#define HISPARSE_HOST_COHERENT    1u   /* fine-grained: GPU accesses bypass its caches */
+#define HISPARSE_HOST_NONCOHERENT 2u   /* coarse-grained: GPU may cache; coherent at kernel boundaries */
+
+typedef struct hisparse_ctx hisparse_ctx;
+
+typedef struct {
+    int32_t top_k;               /* K, 1 <= K <= B, K <= 4096                       */
+    int32_t device_buffer_size;  /* B, 1 <= B <= 16384 (token slots per request)    */
+    int32_t num_layers;          /* layers served by this context                   */
+    int32_t max_requests;        /* R                                               */
+    int32_t max_seq_len;         /* host rows per request                           */
+    int32_t row_bytes;           /* rb, > 0, multiple of 16                          */
+    void* const* host_pool;      /* [num_layers] host pointers, see the layout above;
+                                    each must lie in pinned, GPU-mapped host memory */
+    void* const* hot_buffer;     /* [num_layers] device pointers, [R][B+1][rb]       */
+    const int32_t* anchor_of;    /* [num_layers] host array: the layer whose top-k and
+                                    LRU state this layer shares (== itself for an
+                                    anchor; anchor_of[anchor_of[l]] == anchor_of[l]).
+                                    Skip layers own no LRU state.                    */
+    int32_t block_size;          /* swap-in workgroup size: 0 = default (1024), else a
+                                    multiple of 64 in [128, 1024]                     */
+    int32_t replay_grid;         /* workgroups of the replay kernel: 0 = default     */
+} hisparse_config;
+
+/* One plan row (device): for batch row b, pairs (host position pos[b][m],
+ * device slot slot[b][m]) for m < count[b], in ascending top-k index.  Entries
+ * at m >= count[b] are left as they were.  Layout pos/slot [nb][K], count [nb]. */
+typedef struct {
+    int32_t* pos;
+    int32_t* slot;
+    int32_t* count;
+} hisparse_plan;
+
+/* Create a context: validates the configuration on the host, allocates the
+ * LRU state of every anchor layer ([R][B] lru + [R][B] slot map, int32) and
+ * the error word on the current device.  State starts as if every request
+ * had been admitted with a prompt longer than B.  [vLLM] "Main classes"
+ * (per-cache runtime owning host/hot views, GPU LRU and the fused resolve). */
+int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out);
+
+/* Free the library-owned state.  Caller-owned memory is untouched. */
+void hisparse_destroy(hisparse_ctx* ctx);
+
+/* A request enters decode with host rows [0, seq_len0) valid (the prefill's
+ * KV).  For each i < n, request r = req_ids[i], L0 = seq_len0[i] (device
+ * arrays): the anchor layer's state is reset (lru = 0..B-1; slot map =
+ * identity if L0 <= B, else empty), and when L0 <= B the rows [0, L0) of
+ * every layer sharing this anchor are copied from the host pool into the hot
+ * buffer at slot = position.  [SGL] "Decode Workflow" (fast path: every KV
+ * row already in the buffer). */
+int hisparse_admit(hisparse_ctx* ctx, int32_t anchor_layer, const int32_t* req_ids,
+                   const int32_t* seq_len0, int32_t n, hipStream_t stream);
+
+/* The forward's KV write: new_rows[b] (device, [nb][rb]) goes to the newest
+ * token's row of hot[layer][r]: row L-1 when L <= B, else row B.  Resident
+ * batch rows are skipped.  [SGL] "Decode Workflow" (forward decode, then
+ * eager backup of that token). */
+int hisparse_store_newest(hisparse_ctx* ctx, int32_t layer, const void* new_rows,
+                          const int32_t* seq_lens, const uint8_t* resident_mask,
+                          const int32_t* req_idx, int32_t nb, hipStream_t stream);
+
+/* The fused resolver, one kernel launch.  For every batch row b (topk_idx
+ * [nb][K], seq_lens [nb], resident_mask [nb] or NULL, req_idx [nb] or NULL):
+ *   resident           -> out = topk, nothing else;           [vLLM] resident tier
+ *   L <= B             -> out = topk (slot = position);        [SGL] fast path
+ *   else, per entry i in ascending index:
+ *     -1 -> -1;  L-1 -> B (newest row);
+ *     held in a slot s (hit) -> s, the row does not move;      [SGL] hit detection
+ *     otherwise (miss)  -> taken later;
+ *   LRU reorder: slots not hit keep their order, hit slots keep their prior
+ *   order behind them;                                         [SGL] LRU reorder
+ *   the m-th miss (ascending i) takes the m-th least recent non-hit slot v,
+ *   the slot map records it, the pinned host row is copied into hot[r][v]
+ *   over the host link, and (pos, v) goes to plan_row; loaded slots become
+ *   the most recent, in miss order.                            [vLLM] "Hot lookup and LRU"
+ * plan_row.count[b] = number of misses (0 for resident / fast-path rows).
+ * Uses the anchor layer's state, host pool and hot buffer.  Speculative
+ * verify steps call this once per step on the same state with their own
+ * plan row, consuming each result before the next call.  [vLLM] "Resident
+ * device pages" (verify rows). */
+int hisparse_swap_in(hisparse_ctx* ctx, int32_t anchor_layer,
+                     const int32_t* topk_idx, const int32_t* seq_lens,
+                     const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb,
+                     int32_t* out_slots, hisparse_plan plan_row, hipStream_t stream);
+
+/* Copy-only replay of an anchor's plan row on a skip layer: for each batch
+ * row b and m < count[b], hot[skip][r][slot] <- host[skip][r][pos].  Runs on
+ * a small fixed grid (replay_grid workgroups) so it can overlap other work on
+ * a side stream; the caller orders it after the anchor's swap-in (event) and
+ * before the skip layer's attention.  [SGL] "Shared-index prefetch". */
+int hisparse_replay_plan(hisparse_ctx* ctx, int32_t skip_layer, hisparse_plan plan_row,
+                         const int32_t* req_idx, int32_t nb, hipStream_t side_stream);
+
+/* Eager backup: for every non-resident batch row, host[layer][r][L-1] <-
+ * the newest token's row of hot[layer][r] (row L-1 when L <= B, else B).
+ * Must run after the forward wrote that row and before a later swap-in can
+ * ask for position L-1 from the host pool.  [SGL] "Decode Workflow"
+ * (eager backup). */
+int hisparse_backup(hisparse_ctx* ctx, int32_t layer, const int32_t* seq_lens,
+                    const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb,
+                    hipStream_t stream);
+
+/* Copy an anchor layer's state out of / into the library ([R][B] int32 each,
+ * device pointers).  For tests and checkpointing; asynchronous on stream. */
+int hisparse_get_state(hisparse_ctx* ctx, int32_t anchor_layer, int32_t* lru,
+                       int32_t* slot_tok, hipStream_t stream);
+int hisparse_set_state(hisparse_ctx* ctx, int32_t anchor_layer, const int32_t* lru,
+                       const int32_t* slot_tok, hipStream_t stream);
+
+/* Read (and optionally clear) the device error word.  Synchronizes the
+ * stream: a diagnostic, never part of a decode step. */
+int hisparse_get_error(hisparse_ctx* ctx, uint32_t* flags, int clear, hipStream_t stream);
+
+/* Pinned, GPU-mapped host memory for host pools (flags: HISPARSE_HOST_*). */
+int hisparse_host_alloc(size_t bytes, uint32_t flags, void** out);
+int hisparse_host_free(void* p);
+
+/* Bytes of LDS one swap-in workgroup uses for this configuration. */
+size_t hisparse_swap_in_lds_bytes(int32_t top_k, int32_t device_buffer_size);
+
+const char* hisparse_strerror(int code);
+int hisparse_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HISPARSE_H */

@@ -1,0 +1,70 @@
+"""Drive a decode workload through the CPU oracle.
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark CPU baseline).  The
+step order is the one the pages describe (SGLang guide "HiSparse:
+Hierarchical Sparse Attention", "Decode Workflow": forward, top-k, swap-in,
+attention, eager backup; "Shared-index prefetch": skip layers replay the
+anchor's plan; vLLM design note "HiSparse local KV offload architecture",
+"Resident device pages": verify rows resolved in order, each with its own
+plan row).  Inputs come from the shared seeded generators; nothing here calls
+the HIP library.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional
+
+import numpy as np
+
+from decode_memory_tiering_amd import workload as W
+from oracle.oracle import Oracle, Plan
+
+
+class OracleRun:
+    def __init__(self, wl: W.Workload, steps: Optional[int] = None, lib=None,
+                 host_pools: Optional[List[np.ndarray]] = None):
+        """host_pools: the generated host pool of each layer ([R][max_seq][rb]
+        uint8); copied, so the oracle keeps its own."""
+        self.wl = wl
+        self.steps = wl.steps if steps is None else steps
+        self.max_seq = W.max_seq(wl, self.steps)
+        self.orc = Oracle(num_layers=wl.num_layers, anchor_of=wl.anchor_of, R=wl.R, B=wl.B, K=wl.K,
+                          rb=wl.rb, max_seq=self.max_seq, lib=lib, allocate_host=host_pools is None)
+        if host_pools is not None:
+            self.orc.host = [np.array(p, copy=True) for p in host_pools]
+        else:
+            self._fill_cpu()
+        self.L0 = W.prompt_lens(wl)
+        self.resident = W.resident_mask(wl)
+        for g in wl.anchors:
+            self.orc.admit(g, np.arange(wl.R), self.L0)
+
+    def _fill_cpu(self):
+        import torch
+        for l in range(self.wl.num_layers):
+            t = torch.from_numpy(self.orc.host[l])
+            W.fill_host_pool(t, self.wl, l, W.prompt_lens(self.wl), "cpu")
+
+    def step(self, step: int, topk: Dict[int, np.ndarray], new_kv: np.ndarray):
+        """topk[g]: [S][R][K]; new_kv: [layers][R][rb].  Returns
+        out[g] ([S][R][K]) and plans[g] (list of S plan rows)."""
+        wl, orc = self.wl, self.orc
+        L = W.seq_lens_at(wl, step)
+        res = self.resident if self.resident.any() else None
+        outs: Dict[int, np.ndarray] = {}
+        plans: Dict[int, List[Plan]] = {}
+        for l in range(wl.num_layers):
+            g = wl.anchor_of[l]
+            orc.store_newest(l, new_kv[l], L, res)
+            if g == l:
+                o, p = [], []
+                for s in range(wl.spec):
+                    out, plan = orc.swap_in(l, topk[l][s], L, res)
+                    o.append(out)
+                    p.append(plan)
+                outs[l] = np.stack(o)
+                plans[l] = p
+            else:
+                for s in range(wl.spec):
+                    orc.replay(l, plans[g][s])
+            orc.backup(l, L, res)
+        return outs, plans

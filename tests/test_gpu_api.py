@@ -1,0 +1,258 @@
+"""GPU tests of the C ABI's behaviour beyond the workloads (MI355X only):
+request subsets through the graph-stable mapping, empty batches, device-side
+precondition errors, HIP-graph capture and replay, and the host pool staying
+complete after state is reset mid-run."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from decode_memory_tiering_amd import hisparse as H  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    H.load_library()
+
+
+def _cache(R=8, B=64, K=24, rb=32, max_seq=400, layers=1, anchor_of=(0,), **kw):
+    c = H.HiSparseCache(num_layers=layers, anchor_of=anchor_of, R=R, B=B, K=K, rb=rb, max_seq=max_seq, **kw)
+    rng = np.random.default_rng(0)
+    for l in range(layers):
+        c.host_np[l][:] = rng.integers(0, 256, size=c.host_np[l].shape, dtype=np.uint8)
+    return c
+
+
+def _oracle_for(c):
+    from oracle.oracle import Oracle
+    o = Oracle(num_layers=c.num_layers, anchor_of=c.anchor_of, R=c.R, B=c.B, K=c.K, rb=c.rb, max_seq=c.max_seq)
+    for l in range(c.num_layers):
+        o.host[l][:] = c.host_np[l]
+    return o
+
+
+def _dev(a, dtype=torch.int32):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype)
+
+
+def test_request_subsets_via_req_idx():
+    """Each step only some requests decode, in a shuffled batch order."""
+    R, B, K, rb, max_seq = 10, 64, 24, 32, 600
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
+    o = _oracle_for(c)
+    rng = np.random.default_rng(1)
+    L = rng.integers(30, 300, size=R).astype(np.int32)          # current length per request
+    req = np.arange(R, dtype=np.int32)
+    c.admit(0, _dev(req), _dev(L - 1))
+    o.admit(0, req, L - 1)
+    for step in range(12):
+        nb = int(rng.integers(1, R + 1))
+        idx = rng.permutation(R)[:nb].astype(np.int32)
+        Lb = L[idx]
+        topk = np.stack([rng.choice(int(x), size=K, replace=False) if x >= K else
+                         np.concatenate([rng.permutation(int(x)), -np.ones(K - int(x), np.int64)])
+                         for x in Lb]).astype(np.int32)
+        new = rng.integers(0, 256, size=(nb, rb), dtype=np.uint8)
+        out = torch.empty(nb, K, dtype=torch.int32, device="cuda")
+        plan = H.Plan.empty(nb, K)
+        c.store_newest(0, _dev(new, torch.uint8), _dev(Lb), None, _dev(idx))
+        c.swap_in(0, _dev(topk), _dev(Lb), None, _dev(idx), out, plan)
+        c.backup(0, _dev(Lb), None, _dev(idx))
+        o.store_newest(0, new, Lb, None, idx)
+        eo, ep = o.swap_in(0, topk, Lb, None, idx)
+        o.backup(0, Lb, None, idx)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eo)
+        assert np.array_equal(plan.count.cpu().numpy(), ep.count)
+        lru, tok = c.get_state(0)
+        assert np.array_equal(lru.cpu().numpy(), o.lru[0]) and np.array_equal(tok.cpu().numpy(), o.tok[0])
+        L[idx] += 1
+    assert np.array_equal(c.hot[0].cpu().numpy(), o.hot[0])
+    assert np.array_equal(c.host_np[0], o.host[0])
+    assert c.get_error() == 0
+    c.close()
+
+
+def test_empty_batch_is_a_no_op():
+    c = _cache()
+    z = torch.empty(0, dtype=torch.int32, device="cuda")
+    c.swap_in(0, torch.empty(0, c.K, dtype=torch.int32, device="cuda"), z, None, None,
+              torch.empty(0, c.K, dtype=torch.int32, device="cuda"), H.Plan.empty(0, c.K))
+    c.backup(0, z)
+    c.replay_plan(0, H.Plan.empty(0, c.K))
+    torch.cuda.synchronize()
+    assert c.get_error() == 0
+    c.close()
+
+
+def _slow_setup(c, L0=300):
+    req = torch.arange(c.R, dtype=torch.int32, device="cuda")
+    c.admit(0, req, torch.full((c.R,), L0, dtype=torch.int32, device="cuda"))
+    return L0 + 1
+
+
+@pytest.mark.parametrize("case,flag", [
+    ("duplicate", H.HISPARSE_DERR_TOPK_DUP),
+    ("beyond_L", H.HISPARSE_DERR_TOPK_RANGE),
+    ("below_minus_one", H.HISPARSE_DERR_TOPK_RANGE),
+    ("seq_beyond_pool", H.HISPARSE_DERR_SEQ_LEN),
+    ("req_idx_range", H.HISPARSE_DERR_REQ_IDX),
+])
+def test_bad_rows_fail_alone(case, flag):
+    """A row that breaks a precondition resolves to -1, records no plan, changes
+    no state and sets its error bit; the other rows resolve normally."""
+    R, K = 4, 24
+    c = _cache(R=R, K=K)
+    L = _slow_setup(c)
+    rng = np.random.default_rng(2)
+    topk = np.stack([rng.choice(L, size=K, replace=False) for _ in range(R)]).astype(np.int32)
+    Lb = np.full(R, L, np.int32)
+    idx = np.arange(R, dtype=np.int32)
+    bad = 2
+    if case == "duplicate":
+        topk[bad, 5] = topk[bad, 9]
+    elif case == "beyond_L":
+        topk[bad, 3] = L
+    elif case == "below_minus_one":
+        topk[bad, 3] = -5
+    elif case == "seq_beyond_pool":
+        Lb[bad] = c.max_seq + 1
+    elif case == "req_idx_range":
+        idx[bad] = R + 3
+    lru0, tok0 = c.get_state(0)
+    out = torch.empty(R, K, dtype=torch.int32, device="cuda")
+    plan = H.Plan.empty(R, K)
+    c.swap_in(0, _dev(topk), _dev(Lb), None, _dev(idx), out, plan)
+    torch.cuda.synchronize()
+    assert c.get_error() & flag
+    o = out.cpu().numpy()
+    assert (o[bad] == -1).all() and plan.count[bad].item() == 0
+    lru, tok = c.get_state(0)
+    for r in range(R):
+        if r == bad:
+            continue
+        assert (o[r] >= 0).all() and plan.count[r].item() > 0
+    r_bad = bad if case != "req_idx_range" else None
+    if r_bad is not None:
+        assert torch.equal(lru[r_bad], lru0[r_bad]) and torch.equal(tok[r_bad], tok0[r_bad])
+    assert c.get_error() == 0       # cleared by the previous read
+    c.close()
+
+
+def test_corrupt_state_is_flagged_not_faulted():
+    R, K, B = 2, 24, 64
+    c = _cache(R=R, K=K, B=B)
+    L = _slow_setup(c)
+    lru, tok = c.get_state(0)
+    tok[0, 0] = 5
+    tok[0, 1] = 5                    # two slots claim one position
+    lru[1, 3] = B + 7                # not a slot
+    c.set_state(0, lru, tok)
+    topk = torch.stack([torch.arange(5, 5 + K, dtype=torch.int32)] * R).cuda()
+    out = torch.empty(R, K, dtype=torch.int32, device="cuda")
+    plan = H.Plan.empty(R, K)
+    c.swap_in(0, topk, torch.full((R,), L, dtype=torch.int32, device="cuda"), None, None, out, plan)
+    torch.cuda.synchronize()
+    assert c.get_error() & H.HISPARSE_DERR_STATE
+    assert (out == -1).all() and (plan.count == 0).all()
+    c.close()
+
+
+def test_replay_rejects_bad_plan_entries():
+    c = _cache(layers=2, anchor_of=(0, 0))
+    plan = H.Plan.empty(c.R, c.K)
+    plan.count[0] = c.K + 1
+    plan.count[1] = 1
+    plan.pos[1, 0] = c.max_seq
+    hot0 = c.hot[1].clone()
+    c.replay_plan(1, plan)
+    torch.cuda.synchronize()
+    assert c.get_error() & H.HISPARSE_DERR_PLAN
+    assert torch.equal(c.hot[1], hot0)
+    c.close()
+
+
+def test_graph_capture_and_replay():
+    """store_newest + swap_in + backup captured once in a HIP graph, replayed
+    step after step with new inputs copied into the captured buffers (eager
+    work and synchronisation between replays); every replay must equal the
+    oracle's step."""
+    R, B, K, rb = 6, 128, 40, 48
+    max_seq = 1200
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
+    o = _oracle_for(c)
+    rng = np.random.default_rng(3)
+    L = rng.integers(100, 900, size=R).astype(np.int32)
+    c.admit(0, _dev(np.arange(R)), _dev(L - 1))
+    o.admit(0, np.arange(R), L - 1)
+    topk_buf = torch.zeros(R, K, dtype=torch.int32, device="cuda")
+    L_buf = torch.zeros(R, dtype=torch.int32, device="cuda")
+    new_buf = torch.zeros(R, rb, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(R, K, dtype=torch.int32, device="cuda")
+    plan = H.Plan.empty(R, K)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            c.store_newest(0, new_buf, L_buf)
+            c.swap_in(0, topk_buf, L_buf, None, None, out, plan)
+            c.backup(0, L_buf)
+    torch.cuda.synchronize()
+    for step in range(10):
+        topk = np.stack([rng.choice(int(x), size=K, replace=False) for x in L]).astype(np.int32)
+        new = rng.integers(0, 256, size=(R, rb), dtype=np.uint8)
+        topk_buf.copy_(_dev(topk))
+        L_buf.copy_(_dev(L))
+        new_buf.copy_(_dev(new, torch.uint8))
+        g.replay()
+        _ = (out.sum() + 1).item()            # eager work + sync between replays
+        o.store_newest(0, new, L)
+        eo, ep = o.swap_in(0, topk, L)
+        o.backup(0, L)
+        assert np.array_equal(out.cpu().numpy(), eo), f"replay {step}"
+        assert np.array_equal(plan.count.cpu().numpy(), ep.count)
+        lru, tok = c.get_state(0)
+        assert np.array_equal(lru.cpu().numpy(), o.lru[0]) and np.array_equal(tok.cpu().numpy(), o.tok[0])
+        L = L + 1
+    assert np.array_equal(c.hot[0].cpu().numpy(), o.hot[0])
+    assert np.array_equal(c.host_np[0], o.host[0])
+    assert c.get_error() == 0
+    c.close()
+
+
+def test_readmission_keeps_results_byte_correct():
+    """Resetting a request's state mid-run (admit again) changes slot ids but
+    never the bytes a slot resolves to: the host pool stays complete because
+    every newest token is backed up."""
+    R, B, K, rb = 3, 64, 20, 32
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=500)
+    rng = np.random.default_rng(4)
+    L = np.array([100, 150, 200], np.int32)
+    c.admit(0, _dev(np.arange(R)), _dev(L - 1))
+    for step in range(8):
+        if step == 4:
+            c.admit(0, _dev(np.array([1], np.int32)), _dev(np.array([L[1] - 1], np.int32)))
+        topk = np.stack([rng.choice(int(x), size=K, replace=False) for x in L]).astype(np.int32)
+        new = rng.integers(0, 256, size=(R, rb), dtype=np.uint8)
+        out = torch.empty(R, K, dtype=torch.int32, device="cuda")
+        plan = H.Plan.empty(R, K)
+        c.store_newest(0, _dev(new, torch.uint8), _dev(L))
+        c.swap_in(0, _dev(topk), _dev(L), None, None, out, plan)
+        torch.cuda.synchronize()
+        hot = c.hot[0].cpu().numpy()
+        o = out.cpu().numpy()
+        for r in range(R):
+            for i in range(K):
+                t = topk[r, i]
+                exp = new[r] if t == L[r] - 1 else c.host_np[0][r, t]
+                assert np.array_equal(hot[r, o[r, i]], exp)
+        c.backup(0, _dev(L))
+        torch.cuda.synchronize()
+        L = L + 1
+    assert c.get_error() == 0
+    c.close()

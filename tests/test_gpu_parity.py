@@ -1,0 +1,128 @@
+"""GPU parity: the HIP path against the CPU oracle, bit-exact (MI355X only).
+
+Every test calls the HIP kernels through the C ABI (the Python binding only
+marshals arguments) and compares with the oracle on the same seeded inputs:
+slot ids, plan rows, LRU state and slot map after every step, the pages'
+correctness statement on the gathered rows, and every byte of the hot
+buffers and host pools at the end.  There is no floating point on the path,
+so the bar is exact equality everywhere.
+"""
+import numpy as np
+import pytest
+
+from decode_memory_tiering_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_memory_tiering_amd.hisparse import load_library
+    load_library()  # fails loudly when the HIP library is not built
+
+
+def _lockstep(wl, **kw):
+    from lockstep import run_lockstep
+    print(f"\n[parity] {wl.name} R={wl.R} B={wl.B} K={wl.K} rb={wl.rb} layers={wl.num_layers} "
+          f"steps={kw.get('steps', wl.steps)} block={kw.get('block_size', 0)}", flush=True)
+    st = run_lockstep(wl, **kw)
+    print(f"[parity] {wl.name} ok: {st}", flush=True)
+    return st
+
+
+# -- the five workloads at their full sizes --------------------------------------
+def test_tiny_full():
+    st = _lockstep(W.WORKLOADS["tiny"])
+    assert st["misses"] > 0
+
+
+def test_fastpath_mix_full():
+    st = _lockstep(W.WORKLOADS["fastpath_mix"], progress=True)
+    assert 0 < st["slow_rows"] < 64 * 32
+
+
+@pytest.mark.timeout(900)
+def test_dsv32_decode_full():
+    _lockstep(W.WORKLOADS["dsv32_decode"], progress=True, compare_state_every=4)
+
+
+@pytest.mark.timeout(900)
+def test_indexshare_full_prefetch():
+    _lockstep(W.WORKLOADS["indexshare"], progress=True, prefetch=True, compare_state_every=4)
+
+
+@pytest.mark.timeout(600)
+def test_indexshare_inline_replay():
+    _lockstep(W.WORKLOADS["indexshare"], steps=8, prefetch=False, progress=True)
+
+
+@pytest.mark.timeout(600)
+def test_long_context_full():
+    st = _lockstep(W.WORKLOADS["long_context"], progress=True)
+    assert st["misses"] > 0
+
+
+# -- geometries spanning several tiles with ragged tails, launch shapes --------------
+RAGGED = [
+    W.Workload("ragged_a", 2, (0, 1), R=7, B=1000, K=333, rb=48, steps=12, n_resident=2,
+               seq_first=("uniform", 200, 3000), seed=11),
+    W.Workload("ragged_b", 3, (0, 0, 2), R=5, B=777, K=777, rb=16, steps=10,
+               seq_first=("uniform", 700, 2000), seed=12),
+    W.Workload("ragged_c", 1, (0,), R=9, B=130, K=65, rb=656, steps=20, spec=2,
+               seq_first=("uniform", 60, 600), row_format="fp8_656", seed=13),
+    W.Workload("ragged_d", 1, (0,), R=3, B=4100, K=4096, rb=32, steps=6, topk_kind="uniform",
+               seq_first=("uniform", 4000, 9000), seed=14),
+]
+
+
+def _cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def _launch_shape_fits(wl, block):
+    # 64-entry chunks of the LRU list / top-k row each wave holds in registers
+    waves = block // 64
+    return _cdiv(_cdiv(wl.B, 64), waves) <= 16 and _cdiv(_cdiv(wl.K, 64), waves) <= 4
+
+
+@pytest.mark.parametrize("block", [128, 256, 1024])
+@pytest.mark.parametrize("wl", RAGGED, ids=[w.name for w in RAGGED])
+def test_ragged_geometries(wl, block):
+    if not _launch_shape_fits(wl, block):
+        pytest.skip("buffer too large for this workgroup size (init rejects it)")
+    _lockstep(wl, block_size=block)
+
+
+def test_fast_to_slow_transition():
+    B = 512
+    wl = W.Workload("transition", 1, (0,), R=6, B=B, K=128, rb=64, steps=8,
+                    seq_first=("list", B - 3, B - 1, B, B + 1, B + 2, 2 * B), seed=21)
+    _lockstep(wl)
+
+
+def test_topk_equals_buffer_size():
+    wl = W.Workload("k_eq_b", 1, (0,), R=4, B=256, K=256, rb=32, steps=10,
+                    seq_first=("list", 200, 257, 300, 5000), seed=22)
+    _lockstep(wl)
+
+
+def test_single_slot_buffer():
+    wl = W.Workload("b1", 1, (0,), R=3, B=1, K=1, rb=16, steps=8, topk_kind="uniform",
+                    seq_first=("list", 1, 2, 9), seed=23)
+    _lockstep(wl)
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_host_memory_kinds(flags):
+    _lockstep(W.WORKLOADS["tiny"], steps=6, host_flags=flags)
+
+
+def test_replay_grid_sizes():
+    wl = W.Workload("replay_grid", 4, (0, 0, 0, 0), R=12, B=300, K=100, rb=80, steps=6,
+                    seq_first=("uniform", 200, 5000), seed=24)
+    for g in (1, 5, 64):
+        _lockstep(wl, replay_grid=g, prefetch=True)
