@@ -62,6 +62,29 @@ def measure_link(dev, nbytes=1 << 30):
         hisparse_host_free(p)
 
 
+def counter_traffic(workload):
+    """HBM + host-link bytes per swap-in launch from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or
+    None when there is none for this workload or the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"swap_in_kernel_{workload}_counters.md")
+    src = os.path.join(ROOT, "decode_memory_tiering_amd", "csrc", "hisparse.hip")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "rocprofv3", "`")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("src_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    try:
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, steps, host_pools, topk_all, newkv_all, budget_s=20.0):
     """The oracle, as it stands, on the same inputs: single thread, the first
     steps of the same decode, until about budget_s of oracle time."""
@@ -92,6 +115,11 @@ def main():
     ap.add_argument("--host-flags", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-link", action="store_true")
+    ap.add_argument("--layer-compute-mib", type=int, default=0,
+                    help="stand-in for each layer's other compute: a device copy of this many MiB on the "
+                         "main stream after every layer (the IndexShare overlap case uses 2048)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 5 times (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -107,6 +135,15 @@ def main():
     load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        a = torch.ones(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"calibration_copy_bytes": n, "launches": 5}), flush=True)
+        return
     wl = W.WORKLOADS[args.workload]
     total = args.warmup + args.steps
 
@@ -118,18 +155,27 @@ def main():
     topk_dev = [{a: torch.from_numpy(v).to(dev) for a, v in t.items()} for t in topk_all]
     newkv_dev = [new_kv_all_layers(wl, k, dev) for k in range(total)]
     seq_dev = [g.seq_lens(k) for k in range(total)]
-    counts = [[] for _ in range(total)]
+    # every step records into its own plan count (pos/slot rows are shared), so
+    # nothing but the path runs inside the timed steps
+    from decode_memory_tiering_amd.hisparse import Plan
+    shared = {a: [Plan.empty(wl.R, wl.K, dev) for _ in range(wl.spec)] for a in wl.anchors}
+    step_plans = [{a: [Plan(p.pos, p.slot, torch.zeros(wl.R, dtype=torch.int32, device=dev))
+                       for p in shared[a]] for a in wl.anchors} for _ in range(total)]
     torch.cuda.synchronize(dev)
     log(f"[bench] {wl.name}: setup {time.time() - t_setup:.1f}s")
 
     ev = []   # (start, end) events of every timed swap-in launch
+    between = None
+    if args.layer_compute_mib:
+        n = args.layer_compute_mib << 20
+        csrc = torch.ones(n, dtype=torch.uint8, device=dev)
+        cdst = torch.empty_like(csrc)
+
+        def between(_l):
+            cdst.copy_(csrc)
 
     def run(k, timed):
         main = torch.cuda.current_stream(dev)
-
-        def after(a, s):
-            counts[k].append(g.plans[a][s].count.clone())
-
         if timed:
             # events bracket each swap-in on the stream it is launched on
             orig = g.cache.swap_in
@@ -143,11 +189,11 @@ def main():
                 ev.append((e0, e1))
             g.cache.swap_in = timed_swap_in
             try:
-                g.step(topk_dev[k], newkv_dev[k], seq_dev[k], after_swap_in=after)
+                g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=between)
             finally:
                 g.cache.swap_in = orig
         else:
-            g.step(topk_dev[k], newkv_dev[k], seq_dev[k], after_swap_in=after)
+            g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=between)
 
     for k in range(args.warmup):
         run(k, False)
@@ -159,7 +205,8 @@ def main():
     wall = time.perf_counter() - t0
 
     entries = sum(int(np.count_nonzero(v >= 0)) for k in range(args.warmup, total) for v in topk_all[k].values())
-    misses = sum(int(c.sum().item()) for k in range(args.warmup, total) for c in counts[k])
+    misses = sum(int(p.count.sum().item()) for k in range(args.warmup, total)
+                 for a in wl.anchors for p in step_plans[k][a])
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     mean_launch_s = float(np.mean(launch_ms)) * 1e-3
     miss_bytes_per_launch = misses * wl.rb / len(ev)
@@ -204,6 +251,8 @@ def main():
             "top_k": wl.K, "device_buffer_size": wl.B, "row_bytes": wl.rb, "verify_rows": wl.spec,
             "resident_requests": wl.n_resident, "first_seq_len": list(wl.seq_first),
             "parallelism": "single GPU (requests are independent)",
+            "prefetch": bool(g.prefetch) if wl.skip_layers else None,
+            "layer_compute_mib": args.layer_compute_mib,
         },
         "roofline": {
             "kernel": "swap_in_kernel",
@@ -212,7 +261,7 @@ def main():
             "peak": PCIE5_X16_GBPS,
             "unit": "GB/s",
             "frac": achieved / PCIE5_X16_GBPS,
-            "traffic": None,
+            "traffic": counter_traffic(wl.name),
             "launches": len(ev),
             "mean_launch_us": mean_launch_s * 1e6,
             "miss_bytes_per_launch": miss_bytes_per_launch,

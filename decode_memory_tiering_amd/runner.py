@@ -75,20 +75,22 @@ class GpuRun:
 
     # -- one decode step ------------------------------------------------------
     def step(self, topk: Dict[int, "torch.Tensor"], new_kv: "torch.Tensor", seq_lens,
-             between_layers=None, after_swap_in=None):
+             between_layers=None, after_swap_in=None, plans: Optional[Dict[int, List[Plan]]] = None):
         """topk[g]: [S][R][K] int32 (device) for every anchor g; new_kv:
         [layers][R][rb] uint8 (device); seq_lens: [R] int32 (device).
         between_layers(l) runs on the main stream after layer l (a stand-in for
         the layer's other compute); after_swap_in(g, s) runs right after each
-        swap-in (the consumer of that verify row)."""
+        swap-in (the consumer of that verify row); plans replaces the plan rows
+        this step records into (default: self.plans)."""
         torch, wl, c = self.torch, self.wl, self.cache
+        plans = self.plans if plans is None else plans
         main = torch.cuda.current_stream(self.dev)
         for l in range(wl.num_layers):
             g = wl.anchor_of[l]
             c.store_newest(l, new_kv[l], seq_lens, self.resident)
             if g == l:
                 for s in range(wl.spec):
-                    c.swap_in(l, topk[l][s], seq_lens, self.resident, None, self.out[l][s], self.plans[l][s])
+                    c.swap_in(l, topk[l][s], seq_lens, self.resident, None, self.out[l][s], plans[l][s])
                     if after_swap_in is not None:
                         after_swap_in(l, s)
                 skips = [x for x in wl.skip_layers if wl.anchor_of[x] == l]
@@ -99,7 +101,7 @@ class GpuRun:
                     with torch.cuda.stream(self.side):
                         for x in skips:
                             for s in range(wl.spec):
-                                c.replay_plan(x, self.plans[l][s], None, self.side)
+                                c.replay_plan(x, plans[l][s], None, self.side)
                             e2 = torch.cuda.Event()
                             e2.record(self.side)
                             self.events[x] = e2
@@ -108,7 +110,7 @@ class GpuRun:
                     main.wait_event(self.events.pop(l))
                 else:
                     for s in range(wl.spec):
-                        c.replay_plan(l, self.plans[g][s], None, main)
+                        c.replay_plan(l, plans[g][s], None, main)
             c.backup(l, seq_lens, self.resident)
             if between_layers is not None:
                 between_layers(l)
