@@ -38,7 +38,16 @@ constexpr int kMaxB = 16384;
 constexpr int kMaxK = 4096;
 constexpr int kDefaultBlock = 1024;
 constexpr int kDefaultReplayGrid = 32;
-constexpr int kCopyUnroll = 4;       // 16-byte loads in flight per thread in the copy loops
+// Copy-loop shape: batches of kCopyUnroll 16-byte loads per thread, kCopyBuffers
+// batches in rotation (measured on MI355X; see copy_rows).
+#ifndef HISPARSE_COPY_UNROLL
+#define HISPARSE_COPY_UNROLL 8
+#endif
+#ifndef HISPARSE_COPY_BUFFERS
+#define HISPARSE_COPY_BUFFERS 2
+#endif
+constexpr int kCopyUnroll = HISPARSE_COPY_UNROLL;
+constexpr int kCopyBuffers = HISPARSE_COPY_BUFFERS;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -84,10 +93,18 @@ __device__ int wave_exclusive_scan(int* a, int n)
 }
 
 // Copy `rows` rows of rb bytes (rb % 16 == 0) from src rows to dst rows, the
-// row numbers given by src_row(m) / dst_row(m); chunk c of the flattened
-// (row, 16-byte column) space goes to thread c % nthr.  kCopyUnroll loads are
-// issued before their stores so that enough host-link reads are in flight.
-template <typename SrcRow, typename DstRow>
+// row numbers given by src_row(m) / dst_row(m).  Chunk c of the flattened
+// (row, 16-byte column) space goes to thread c % nthr; the (row, column) walk
+// is incremental, so no chunk needs a division.
+//
+// Software-pipelined over NB rotating register batches of U 16-byte loads:
+// batch p is stored while the loads of the following NB-1 batches are in
+// flight.  Rotating (not copying) the batches matters: moving a register that
+// a load has not filled yet, or loading into one whose store is still
+// pending, makes the compiler drain the loads.  Loads are never predicated
+// for the same reason: a chunk past the end reads 16 bytes of dst instead
+// (device memory) and the value is dropped.
+template <int U, int NB, typename SrcRow, typename DstRow>
 __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                           int rows, int rb, int tid, int nthr,
                                           SrcRow src_row, DstRow dst_row)
@@ -95,31 +112,46 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8
     const int cpr = rb >> 4;
     const int total = rows * cpr;
     if (tid >= total) return;
-    int row = tid / cpr, col = tid - (tid / cpr) * cpr;
-    const int drow = nthr / cpr, dcol = nthr - (nthr / cpr) * cpr;
-    for (int base = tid; base < total; base += kCopyUnroll * nthr) {
-        u32x4 v[kCopyUnroll];
-        int rr[kCopyUnroll], cc[kCopyUnroll];
+    const int drow = nthr / cpr, dcol = nthr - drow * cpr;
+    const int last = rows - 1;
+    int row = tid / cpr, col = tid - row * cpr;   // position of the next chunk to load
+    int c = tid;                                  // its flat index
+
+    u32x4 v[NB][U];
+    int vr[NB][U], vc[NB][U];
+    auto load_batch = [&](int p) {
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
-            rr[u] = row;
-            cc[u] = col;
-            if (base + u * nthr < total) {
-                const u32x4* p = reinterpret_cast<const u32x4*>(
-                    src + static_cast<size_t>(src_row(row)) * rb + (static_cast<size_t>(col) << 4));
-                v[u] = __builtin_nontemporal_load(p);
-            }
+        for (int u = 0; u < U; ++u) {
+            const bool in = c < total;
+            const int rr = in ? row : last;       // keeps src_row's index in range
+            const uint8_t* q = src + static_cast<size_t>(src_row(rr)) * rb + (static_cast<size_t>(col) << 4);
+            v[p][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in ? q : dst));
+            vr[p][u] = row;
+            vc[p][u] = col;
+            c += nthr;
             col += dcol;
             row += drow;
             if (col >= cpr) { col -= cpr; ++row; }
         }
+    };
+    auto store_batch = [&](int p, int base) {
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
-            if (base + u * nthr < total) {
-                u32x4* q = reinterpret_cast<u32x4*>(
-                    dst + static_cast<size_t>(dst_row(rr[u])) * rb + (static_cast<size_t>(cc[u]) << 4));
-                *q = v[u];
-            }
+        for (int u = 0; u < U; ++u) {
+            if (base + u * nthr < total)
+                *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(dst_row(vr[p][u])) * rb +
+                                          (static_cast<size_t>(vc[p][u]) << 4)) = v[p][u];
+        }
+    };
+
+#pragma unroll
+    for (int p = 0; p < NB - 1; ++p) load_batch(p);
+    for (int base = tid;;) {
+#pragma unroll
+        for (int p = 0; p < NB; ++p) {
+            load_batch((p + NB - 1) % NB);
+            store_batch(p, base);
+            base += U * nthr;
+            if (base >= total) return;
         }
     }
 }
@@ -144,30 +176,30 @@ struct SwapInArgs {
     int32_t R, B, K, rb, max_seq, hash_bits;
 };
 
+constexpr unsigned long long kHashEmpty = ~0ull;
+
 struct SwapInLds {
-    int* hash;      // [1 << hash_bits]  top-k index of a candidate position, -1 empty
-    int* topk_s;    // [K]
+    unsigned long long* hash;  // [1 << hash_bits]  (position << 32) | top-k index; kHashEmpty = free
     int* out_s;     // [K]   -1 / B / slot of a hit / kMissMark
     int* plan_t;    // [K]   m-th miss: host position
     int* plan_v;    // [K]   m-th least recent non-hit slot (victim of the m-th miss)
     int* cnt_b;     // [ceil(B/64)]  hits per 64-entry chunk of the LRU list, then prefix
     int* cnt_k;     // [ceil(K/64)]  misses per 64-entry chunk of the top-k row, then prefix
-    int* totals;    // [2]   hits, misses
+    int* totals;    // [4]   hits, misses
     uint8_t* hit;   // [B]   slot was hit this step
 };
 
 __host__ __device__ inline size_t swap_in_lds_bytes_impl(int B, int K, int hash_bits)
 {
-    const size_t ints = (size_t(1) << hash_bits) + 4 * size_t(K) + (B + 63) / 64 + (K + 63) / 64 + 4;
-    return ints * 4 + ((size_t(B) + 3) & ~size_t(3));
+    const size_t ints = 3 * size_t(K) + (B + 63) / 64 + (K + 63) / 64 + 4;
+    return (size_t(1) << hash_bits) * 8 + ints * 4 + ((size_t(B) + 3) & ~size_t(3));
 }
 
-__device__ inline SwapInLds carve_lds(int* smem, int B, int K, int hash_bits)
+__device__ inline SwapInLds carve_lds(unsigned long long* smem, int B, int K, int hash_bits)
 {
     SwapInLds s;
     s.hash = smem;
-    s.topk_s = s.hash + (1 << hash_bits);
-    s.out_s = s.topk_s + K;
+    s.out_s = reinterpret_cast<int*>(s.hash + (size_t(1) << hash_bits));
     s.plan_t = s.out_s + K;
     s.plan_v = s.plan_t + K;
     s.cnt_b = s.plan_v + K;
@@ -190,7 +222,7 @@ __device__ void fail_row(const SwapInArgs& a, int b, uint32_t flags)
 template <int EB, int EK>
 __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
 {
-    extern __shared__ int smem[];
+    extern __shared__ unsigned long long smem[];
     const int b = blockIdx.x;
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nthr / kWave;
@@ -216,26 +248,43 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
     int32_t* lru = a.lru + size_t(r) * B;
     int32_t* tok = a.tok + size_t(r) * B;
 
-    // -- classify the top-k row ------------------------------------------
-    for (int h = tid; h < (1 << a.hash_bits); h += nthr) s.hash[h] = -1;
+    // Every global read of the resolve is issued here, before any barrier,
+    // so the whole pass waits on one memory latency.  Entry e of chunk
+    // c = k * nwaves + wave is e = c * 64 + lane (top-k row, slot map and
+    // LRU list alike).
+    // (The LRU list is read here only when the registers allow it; the
+    // largest buffers read it after the probe instead of spilling.)
+    constexpr bool kEarlyLru = EB <= 8;
+    int t_own[EK], tok_own[EB], lru_own[EB];
+#pragma unroll
+    for (int k = 0; k < EK; ++k) {
+        const int c = k * nwaves + wave, i = c * kWave + lane;
+        t_own[k] = (c < nck && i < K) ? topk[i] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < EB; ++k) {
+        const int c = k * nwaves + wave, x = c * kWave + lane;
+        const bool in = c < ncb && x < B;
+        tok_own[k] = in ? tok[x] : -1;
+        lru_own[k] = (kEarlyLru && in) ? lru[x] : 0;
+    }
+    for (int h = tid; h <= hmask; h += nthr) s.hash[h] = kHashEmpty;
     for (int x = tid; x < B; x += nthr) s.hit[x] = 0;
-    int t_own[EK];
+
+    // -- classify the top-k row ------------------------------------------
     uint32_t err = 0;
 #pragma unroll
     for (int k = 0; k < EK; ++k) {
         const int c = k * nwaves + wave, i = c * kWave + lane;
-        int t = -1;
         if (c < nck && i < K) {
-            t = topk[i];
+            const int t = t_own[k];
             int cls;
             if (t == -1) cls = -1;
             else if (t < -1 || t >= L) { cls = -1; err |= HISPARSE_DERR_TOPK_RANGE; }
             else if (t == L - 1) cls = B;          // newest token: its own row
             else cls = kMissMark;
-            s.topk_s[i] = t;
             s.out_s[i] = cls;
         }
-        t_own[k] = t;
     }
     __syncthreads();
 
@@ -245,11 +294,16 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
         const int c = k * nwaves + wave, i = c * kWave + lane;
         const int t = t_own[k];
         if (c < nck && i < K && t >= 0 && t < L - 1) {
+            const unsigned long long e = (static_cast<unsigned long long>(static_cast<uint32_t>(t)) << 32) |
+                                         static_cast<uint32_t>(i);
             uint32_t h = hash_slot(t, a.hash_bits);
-            for (;;) {   // the table has at least 2K entries, so an empty one is always reached
-                const int prev = atomicCAS(&s.hash[h], -1, i);
-                if (prev == -1) break;
-                if (s.topk_s[prev] == t) { err |= HISPARSE_DERR_TOPK_DUP; break; }
+            for (;;) {   // the table has at least 4K entries, so a free one is always reached
+                const unsigned long long prev = atomicCAS(&s.hash[h], kHashEmpty, e);
+                if (prev == kHashEmpty) break;
+                if (static_cast<uint32_t>(prev >> 32) == static_cast<uint32_t>(t)) {
+                    err |= HISPARSE_DERR_TOPK_DUP;
+                    break;
+                }
                 h = (h + 1) & hmask;
             }
         }
@@ -260,40 +314,64 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
     }
 
     // -- hit detection: probe every slot's position ----------------------
-    for (int x = tid; x < B; x += nthr) {
-        const int t = tok[x];
-        if (t >= 0 && t < L - 1) {
-            uint32_t h = hash_slot(t, a.hash_bits);
-            for (;;) {
-                const int i = s.hash[h];
-                if (i < 0) break;
-                if (s.topk_s[i] == t) {
+    // A thread's probes advance in lockstep, one table entry per round, in
+    // groups of up to 8 chains, so their LDS reads overlap instead of running
+    // one chain after another.
+    constexpr int kG = EB < 8 ? EB : 8;
+#pragma unroll
+    for (int g0 = 0; g0 < EB; g0 += kG) {
+        uint32_t h[kG];
+        uint32_t pending = 0;
+#pragma unroll
+        for (int q = 0; q < kG; ++q) {
+            const int k = g0 + q;
+            const int c = k * nwaves + wave, x = c * kWave + lane;
+            const int t = tok_own[k];
+            h[q] = 0;
+            if (c < ncb && x < B) {
+                if (t >= 0 && t < L - 1) {
+                    h[q] = hash_slot(t, a.hash_bits);
+                    pending |= 1u << q;
+                } else if (t < -1 || t >= a.max_seq) {
+                    err |= HISPARSE_DERR_STATE;
+                }
+            }
+        }
+        while (pending) {   // ends: every chain stops at a free entry, and the table is at most half full
+#pragma unroll
+            for (int q = 0; q < kG; ++q) {
+                if (!((pending >> q) & 1u)) continue;
+                const int k = g0 + q;
+                const unsigned long long e = s.hash[h[q]];
+                if (e == kHashEmpty) {
+                    pending &= ~(1u << q);
+                } else if (static_cast<uint32_t>(e >> 32) == static_cast<uint32_t>(tok_own[k])) {
+                    const int x = (k * nwaves + wave) * kWave + lane;
+                    const int i = static_cast<int>(static_cast<uint32_t>(e));
                     if (atomicCAS(&s.out_s[i], kMissMark, x) == kMissMark) s.hit[x] = 1;
                     else err |= HISPARSE_DERR_STATE;   // two slots claim one position
-                    break;
+                    pending &= ~(1u << q);
+                } else {
+                    h[q] = (h[q] + 1) & hmask;
                 }
-                h = (h + 1) & hmask;
             }
-        } else if (t < -1 || t >= a.max_seq) {
-            err |= HISPARSE_DERR_STATE;
         }
     }
     __syncthreads();
 
     // -- ballots: hits along the LRU list, misses along the top-k row ----
-    int s_own[EB], lp_b[EB];
+    int lp_b[EB];
     uint32_t hbits = 0;
 #pragma unroll
     for (int k = 0; k < EB; ++k) {
         const int c = k * nwaves + wave, j = c * kWave + lane;
-        s_own[k] = 0;
         lp_b[k] = 0;
         if (c < ncb) {
             bool f = false;
             if (j < B) {
-                int x = lru[j];
+                int x = kEarlyLru ? lru_own[k] : lru[j];
                 if (x < 0 || x >= B) { err |= HISPARSE_DERR_STATE; x = 0; }
-                s_own[k] = x;
+                lru_own[k] = x;
                 f = s.hit[x] != 0;
             }
             const uint64_t m = __ballot(f);
@@ -346,7 +424,7 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
         const int c = k * nwaves + wave, j = c * kWave + lane;
         if (c < ncb && j < B) {
             const int hits_before = s.cnt_b[c] + lp_b[k];
-            const int x = s_own[k];
+            const int x = lru_own[k];
             int pos;
             if ((hbits >> k) & 1u) {
                 pos = n_keep - M + hits_before;
@@ -396,8 +474,8 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
     uint8_t* dst = a.hot + size_t(r) * (B + 1) * a.rb;
     const int* pt = s.plan_t;
     const int* pv = s.plan_v;
-    copy_rows(src, dst, M, a.rb, tid, nthr,
-              [pt](int m) { return pt[m]; }, [pv](int m) { return pv[m]; });
+    copy_rows<kCopyUnroll, kCopyBuffers>(src, dst, M, a.rb, tid, nthr,
+                           [pt](int m) { return pt[m]; }, [pv](int m) { return pv[m]; });
 }
 
 // ---------------------------------------------------------------------------
@@ -444,7 +522,7 @@ __global__ __launch_bounds__(256) void replay_kernel(ReplayArgs a)
             if (threadIdx.x == 0) atomicOr(a.err, HISPARSE_DERR_PLAN);
             continue;
         }
-        copy_rows(a.host + size_t(r) * a.max_seq * a.rb, a.hot + size_t(r) * (a.B + 1) * a.rb,
+        copy_rows<kCopyUnroll, kCopyBuffers>(a.host + size_t(r) * a.max_seq * a.rb, a.hot + size_t(r) * (a.B + 1) * a.rb,
                   cnt, a.rb, threadIdx.x, blockDim.x,
                   [pos](int m) { return pos[m]; }, [slot](int m) { return slot[m]; });
         __syncthreads();
@@ -570,12 +648,17 @@ SwapInFn pick_kernel(int eb, int ek)
     return nullptr;
 }
 
-int hash_bits_for(int K)
+// Open-addressed LDS table: 4K entries (load factor at most 1/4, short probe
+// chains) when that fits the workgroup's LDS budget, else 2K (at most 1/2).
+int hash_bits_for(int K, int B, size_t lds_budget)
 {
-    int bits = 1;
-    while ((1 << bits) < 2 * K) ++bits;
+    int bits = 2;
+    while ((1 << bits) < 4 * K) ++bits;
+    if (swap_in_lds_bytes_impl(B, K, bits) > lds_budget) --bits;
     return bits;
 }
+
+constexpr size_t kGfx950LdsPerWorkgroup = 160 * 1024;
 
 }  // namespace
 
@@ -638,7 +721,8 @@ int hisparse_version(void) { return 1; }
 size_t hisparse_swap_in_lds_bytes(int32_t top_k, int32_t device_buffer_size)
 {
     if (top_k <= 0 || device_buffer_size <= 0) return 0;
-    return swap_in_lds_bytes_impl(device_buffer_size, top_k, hash_bits_for(top_k));
+    return swap_in_lds_bytes_impl(device_buffer_size, top_k,
+                                  hash_bits_for(top_k, device_buffer_size, kGfx950LdsPerWorkgroup));
 }
 
 const char* hisparse_strerror(int code)
@@ -692,7 +776,7 @@ int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out)
     c->K = K; c->B = B; c->layers = cfg->num_layers; c->R = cfg->max_requests;
     c->max_seq = cfg->max_seq_len; c->rb = cfg->row_bytes;
     c->block = block; c->replay_grid = replay_grid;
-    c->hash_bits = hash_bits_for(K);
+
     c->anchor_of.assign(cfg->anchor_of, cfg->anchor_of + cfg->num_layers);
     auto fail = [&](int rc) { hisparse_destroy(c); return rc; };
 
@@ -715,10 +799,11 @@ int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out)
     const int ek = ((K + 63) / 64 + nwaves - 1) / nwaves;
     c->swap_in_fn = pick_kernel(eb, ek);
     if (!c->swap_in_fn) return fail(HISPARSE_EINVAL);
-    c->lds = swap_in_lds_bytes_impl(B, K, c->hash_bits);
     int max_lds = 0;
     if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device) != hipSuccess)
         return fail(HISPARSE_EHIP(hipGetLastError()));
+    c->hash_bits = hash_bits_for(K, B, size_t(max_lds));
+    c->lds = swap_in_lds_bytes_impl(B, K, c->hash_bits);
     if (c->lds > size_t(max_lds)) return fail(HISPARSE_EINVAL);
     if (c->lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(c->swap_in_fn),

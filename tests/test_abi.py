@@ -43,7 +43,7 @@ def test_pure_host_calls(lib):
     assert H.hisparse_strerror(0) == "ok"
     assert H.hisparse_strerror(-22) == "invalid argument"
     b = H.hisparse_swap_in_lds_bytes(2048, 6144)
-    assert 40_000 < b < 64 * 1024
+    assert 40_000 < b <= 160 * 1024          # fits one gfx950 workgroup
     assert H.hisparse_swap_in_lds_bytes(0, 10) == 0
 
 
