@@ -37,7 +37,7 @@ constexpr int kMissMark = INT_MIN;   // out_s value of an entry still waiting fo
 constexpr int kMaxB = 16384;
 constexpr int kMaxK = 4096;
 constexpr int kDefaultBlock = 1024;
-constexpr int kDefaultReplayGrid = 32;
+constexpr int kDefaultReplayGrid = 12;   // enough to fill the host link without crowding the fabric (measured)
 // Copy-loop shape: batches of kCopyUnroll 16-byte loads per thread, kCopyBuffers
 // batches in rotation (measured on MI355X; see copy_rows).
 #ifndef HISPARSE_COPY_UNROLL
@@ -47,6 +47,7 @@ constexpr int kDefaultReplayGrid = 32;
 #define HISPARSE_COPY_BUFFERS 2
 #endif
 constexpr int kCopyUnroll = HISPARSE_COPY_UNROLL;
+constexpr int kReplayStage = 2048;   // plan rows staged in LDS per replay block
 constexpr int kCopyBuffers = HISPARSE_COPY_BUFFERS;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -104,10 +105,14 @@ __device__ int wave_exclusive_scan(int* a, int n)
 // pending, makes the compiler drain the loads.  Loads are never predicated
 // for the same reason: a chunk past the end reads 16 bytes of dst instead
 // (device memory) and the value is dropped.
-template <int U, int NB, typename SrcRow, typename DstRow>
+struct KeepAll {
+    __device__ bool operator()(int) const { return true; }
+};
+
+template <int U, int NB, typename SrcRow, typename DstRow, typename Keep = KeepAll>
 __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                           int rows, int rb, int tid, int nthr,
-                                          SrcRow src_row, DstRow dst_row)
+                                          SrcRow src_row, DstRow dst_row, Keep keep = Keep())
 {
     const int cpr = rb >> 4;
     const int total = rows * cpr;
@@ -137,7 +142,7 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8
     auto store_batch = [&](int p, int base) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (base + u * nthr < total)
+            if (base + u * nthr < total && keep(vr[p][u]))
                 *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(dst_row(vr[p][u])) * rb +
                                           (static_cast<size_t>(vc[p][u]) << 4)) = v[p][u];
         }
@@ -154,6 +159,20 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8
             if (base >= total) return;
         }
     }
+}
+
+// Replay's variant: row m goes from host row src_row[m] to hot row
+// dst_row[m] (both absolute, from LDS); a row marked -1 is not copied (its
+// load reads host row 0, which always exists, and is dropped).
+__device__ __forceinline__ void copy_rows_staged(const uint8_t* __restrict__ host, uint8_t* __restrict__ hot,
+                                                 const long long* src_row, const int* dst_row,
+                                                 int rows, int rb, int tid, int nthr)
+{
+    copy_rows<kCopyUnroll, kCopyBuffers>(
+        host, hot, rows, rb, tid, nthr,
+        [src_row](int m) { return src_row[m] < 0 ? 0ll : src_row[m]; },
+        [dst_row](int m) { return dst_row[m] < 0 ? 0 : dst_row[m]; },
+        [dst_row](int m) { return dst_row[m] >= 0; });
 }
 
 // ---------------------------------------------------------------------------
@@ -492,40 +511,99 @@ struct ReplayArgs {
     int32_t nb, R, B, K, rb, max_seq;
 };
 
-// Small fixed grid: workgroup w takes batch rows w, w + grid, ...
+// Small fixed grid.  The plan's rows, across all batch rows, are numbered
+// 0..total-1 (an exclusive prefix of the counts, computed by every workgroup
+// in LDS), and the flattened (row, 16-byte column) space is split evenly over
+// the grid: each workgroup copies one contiguous range, so the grid stays
+// busy until the end whatever the counts are.  A row with an invalid count or
+// request index is skipped as a whole, a pair out of range on its own; both
+// set the error word.
 __global__ __launch_bounds__(256) void replay_kernel(ReplayArgs a)
 {
-    for (int b = blockIdx.x; b < a.nb; b += gridDim.x) {
+    extern __shared__ int start[];           // [nb + 1] first flattened row of each batch row; [nb] = total
+    __shared__ int wave_total[1024 / kWave];
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+
+    // -- exclusive prefix of the valid counts over the batch ------------------
+    const int seg = (a.nb + nthr - 1) / nthr;
+    int mine = 0;
+    uint32_t flags = 0;
+    for (int q = 0; q < seg; ++q) {
+        const int b = tid * seg + q;
+        if (b >= a.nb) break;
+        int cnt = a.count[b];
         const int r = a.req_idx ? a.req_idx[b] : b;
-        const int cnt = a.count[b];
-        if (r < 0 || r >= a.R) {
-            if (threadIdx.x == 0) atomicOr(a.err, HISPARSE_DERR_REQ_IDX);
-            continue;
+        if (r < 0 || r >= a.R) { flags |= HISPARSE_DERR_REQ_IDX; cnt = 0; }
+        else if (cnt < 0 || cnt > a.K) { flags |= HISPARSE_DERR_PLAN; cnt = 0; }
+        start[b] = cnt;
+        mine += cnt;
+    }
+    if (flags && blockIdx.x == 0) atomicOr(a.err, flags);
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += y;
+    }
+    if (lane == kWave - 1) wave_total[wave] = incl;
+    __syncthreads();
+    int run = incl - mine, total_rows = 0;
+    for (int w = 0; w < nthr / kWave; ++w) {
+        const int t = wave_total[w];
+        if (w < wave) run += t;
+        total_rows += t;
+    }
+    for (int q = 0; q < seg; ++q) {
+        const int b = tid * seg + q;
+        if (b >= a.nb) break;
+        const int cnt = start[b];
+        start[b] = run;
+        run += cnt;
+    }
+    if (tid == 0) start[a.nb] = total_rows;
+    __syncthreads();
+
+    // -- this workgroup's range of plan rows, in LDS-staged blocks ----------
+    // Rows are split evenly over the grid; each block of up to kReplayStage
+    // rows has its (host row, hot row) pairs gathered into LDS with coalesced
+    // reads, then copied by the same pipelined loop as the swap-in's misses.
+    const int per = (total_rows + gridDim.x - 1) / gridDim.x;
+    const int row_lo = per * blockIdx.x;
+    const int row_hi = row_lo + per < total_rows ? row_lo + per : total_rows;
+    long long* src_row = reinterpret_cast<long long*>(start + ((a.nb + 2) & ~1));   // 8-byte aligned
+    int* dst_row = reinterpret_cast<int*>(src_row + kReplayStage);
+    int b = 0;                               // batch row holding row_lo
+    for (int lo_b = 0, hi_b = a.nb - 1; lo_b < hi_b;) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if (start[mid] <= row_lo) lo_b = mid; else hi_b = mid - 1;
+        b = lo_b;
+    }
+    for (int f0 = row_lo; f0 < row_hi; f0 += kReplayStage) {
+        const int n = row_hi - f0 < kReplayStage ? row_hi - f0 : kReplayStage;
+        // every thread walks b forward to its row; rows are consecutive, so
+        // the walk per thread is short
+        int bt = b;
+        for (int q = tid; q < n; q += nthr) {
+            const int f = f0 + q;
+            while (bt + 1 < a.nb && start[bt + 1] <= f) ++bt;
+            const int m = f - start[bt];
+            const int r = a.req_idx ? a.req_idx[bt] : bt;
+            const int t = a.pos[size_t(bt) * a.K + m];
+            const int v = a.slot[size_t(bt) * a.K + m];
+            if (t < 0 || t >= a.max_seq || v < 0 || v >= a.B) {
+                atomicOr(a.err, HISPARSE_DERR_PLAN);
+                src_row[q] = -1;             // skipped: copied onto itself below
+                dst_row[q] = -1;
+            } else {
+                src_row[q] = static_cast<long long>(r) * a.max_seq + t;
+                dst_row[q] = r * (a.B + 1) + v;
+            }
         }
-        if (cnt <= 0) {
-            if (cnt < 0 && threadIdx.x == 0) atomicOr(a.err, HISPARSE_DERR_PLAN);
-            continue;
-        }
-        if (cnt > a.K) {
-            if (threadIdx.x == 0) atomicOr(a.err, HISPARSE_DERR_PLAN);
-            continue;
-        }
-        const int32_t* pos = a.pos + size_t(b) * a.K;
-        const int32_t* slot = a.slot + size_t(b) * a.K;
-        // every pair must address rows inside the pool and the buffer
-        bool bad = false;
-        for (int m = threadIdx.x; m < cnt; m += blockDim.x) {
-            const int t = pos[m], v = slot[m];
-            if (t < 0 || t >= a.max_seq || v < 0 || v >= a.B) bad = true;
-        }
-        if (__syncthreads_or(bad)) {
-            if (threadIdx.x == 0) atomicOr(a.err, HISPARSE_DERR_PLAN);
-            continue;
-        }
-        copy_rows<kCopyUnroll, kCopyBuffers>(a.host + size_t(r) * a.max_seq * a.rb, a.hot + size_t(r) * (a.B + 1) * a.rb,
-                  cnt, a.rb, threadIdx.x, blockDim.x,
-                  [pos](int m) { return pos[m]; }, [slot](int m) { return slot[m]; });
         __syncthreads();
+        copy_rows_staged(a.host, a.hot, src_row, dst_row, n, a.rb, tid, nthr);
+        __syncthreads();
+        while (b + 1 < a.nb && start[b + 1] <= f0 + n) ++b;
     }
 }
 
@@ -659,6 +737,13 @@ int hash_bits_for(int K, int B, size_t lds_budget)
 }
 
 constexpr size_t kGfx950LdsPerWorkgroup = 160 * 1024;
+
+// Dynamic LDS of the replay kernel: the prefix of the plan counts (padded to
+// 8 bytes), then one staged block of (host row, hot row) pairs.
+size_t replay_lds_bytes(int nb)
+{
+    return size_t((nb + 2) & ~1) * sizeof(int) + size_t(kReplayStage) * (sizeof(long long) + sizeof(int));
+}
 
 }  // namespace
 
@@ -805,6 +890,13 @@ int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out)
     c->hash_bits = hash_bits_for(K, B, size_t(max_lds));
     c->lds = swap_in_lds_bytes_impl(B, K, c->hash_bits);
     if (c->lds > size_t(max_lds)) return fail(HISPARSE_EINVAL);
+    const size_t rlds = replay_lds_bytes(c->R) + 16 * sizeof(int);
+    if (rlds > size_t(max_lds)) return fail(HISPARSE_EINVAL);
+    if (rlds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&replay_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(replay_lds_bytes(c->R)));
+        if (e != hipSuccess) return fail(HISPARSE_EHIP(e));
+    }
     if (c->lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(c->swap_in_fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(c->lds));
@@ -899,8 +991,7 @@ int hisparse_replay_plan(hisparse_ctx* c, int32_t skip_layer, hisparse_plan plan
     a.pos = plan_row.pos; a.slot = plan_row.slot; a.count = plan_row.count; a.req_idx = req_idx;
     a.host = c->host[skip_layer]; a.hot = c->hot[skip_layer]; a.err = c->err;
     a.nb = nb; a.R = c->R; a.B = c->B; a.K = c->K; a.rb = c->rb; a.max_seq = c->max_seq;
-    const int grid = nb < c->replay_grid ? nb : c->replay_grid;
-    hipLaunchKernelGGL(replay_kernel, dim3(grid), dim3(256), 0, side_stream, a);
+    hipLaunchKernelGGL(replay_kernel, dim3(c->replay_grid), dim3(256), replay_lds_bytes(nb), side_stream, a);
     return hip_rc(hipGetLastError());
 }
 

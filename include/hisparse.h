@@ -170,7 +170,11 @@ int hisparse_swap_in(hisparse_ctx* ctx, int32_t anchor_layer,
  * row b and m < count[b], hot[skip][r][slot] <- host[skip][r][pos].  Runs on
  * a small fixed grid (replay_grid workgroups) so it can overlap other work on
  * a side stream; the caller orders it after the anchor's swap-in (event) and
- * before the skip layer's attention.  [SGL] "Shared-index prefetch". */
+ * before the skip layer's attention.  The grid splits the plan's rows evenly,
+ * whatever the per-row counts.  A batch row with a count outside [0, K] or a
+ * request index outside [0, R) is skipped, and so is a single (pos, slot)
+ * pair outside the pool or the buffer; each sets HISPARSE_DERR_PLAN or
+ * HISPARSE_DERR_REQ_IDX.  [SGL] "Shared-index prefetch". */
 int hisparse_replay_plan(hisparse_ctx* ctx, int32_t skip_layer, hisparse_plan plan_row,
                          const int32_t* req_idx, int32_t nb, hipStream_t side_stream);
 
