@@ -49,6 +49,7 @@
 
 #include <stdlib.h>
 #include <string.h>
+#include <stdint.h>
 
 int32_t orc_newest_row(int32_t B, int32_t L)
 {
@@ -272,6 +273,114 @@ int orc_swap_in(int32_t R, int32_t B, int32_t K, int64_t rb, int32_t max_seq,
             return ORC_EINVAL;
         int rc = orc_swap_in_row(
             B, K, rb, max_seq, seq_lens[b], resident_mask ? resident_mask[b] : 0,
+            topk + (int64_t)b * K, out + (int64_t)b * K,
+            lru + (int64_t)r * B, tok + (int64_t)r * B,
+            host + (int64_t)r * max_seq * rb, hot + (int64_t)r * (B + 1) * rb,
+            plan_pos + (int64_t)b * K, plan_slot + (int64_t)b * K, plan_count + b);
+        if (rc != ORC_OK)
+            return rc;
+    }
+    return ORC_OK;
+}
+
+/* Per-page residency (vLLM design note, "Resident device pages" and "Hot
+ * lookup and LRU": a resident page is checked first and resolves to its
+ * resident physical row, before any hot lookup or host copy; pages that are
+ * not resident are host-backed holes served by the hot buffer).
+ *
+ * block_row[p] is the physical page holding positions [p*P, (p+1)*P) of this
+ * request, or -1 for a host-backed page; pages at or beyond max_pages are
+ * host-backed.  Output ids live in one row space chosen by the caller:
+ *   resident position t  ->  block_row[t / P] * P + t % P
+ *   hot row s (0..B)     ->  hot_base + s
+ *   padding              ->  -1
+ * The resident entries are taken out of the row (replaced by padding, which
+ * the hot tiers ignore) and the rest is resolved exactly as orc_swap_in_row
+ * does, so resident positions never touch the LRU state, the plan or the
+ * hot buffer. */
+int orc_swap_in_row_paged(int32_t B, int32_t K, int64_t rb, int32_t max_seq,
+                          int32_t L, const int32_t* block_row, int32_t max_pages,
+                          int32_t page_size, int64_t hot_base,
+                          const int32_t* topk, int32_t* out,
+                          int32_t* lru, int32_t* tok,
+                          const uint8_t* host_req, uint8_t* hot_req,
+                          int32_t* plan_pos, int32_t* plan_slot, int32_t* plan_count)
+{
+    if (B <= 0 || K <= 0 || K > B || page_size <= 0 || max_pages < 0 || hot_base < 0 ||
+        !topk || !out || !plan_count || (max_pages > 0 && !block_row))
+        return ORC_EINVAL;
+    if (L < 1 || L > max_seq)
+        return ORC_EPRECOND;
+    int rc = check_topk(K, L, topk);
+    if (rc != ORC_OK)
+        return rc;
+
+    int32_t* hot_row = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+    int64_t* res_row = (int64_t*)malloc(sizeof(int64_t) * (size_t)K);
+    if (!hot_row || !res_row) {
+        free(hot_row); free(res_row);
+        return ORC_ENOMEM;
+    }
+    /* Tier 0, per entry: is the position's page resident? */
+    for (int32_t i = 0; i < K; ++i) {
+        int32_t t = topk[i];
+        res_row[i] = -1;
+        hot_row[i] = t;
+        if (t < 0)
+            continue;
+        int32_t pg = t / page_size;
+        int32_t phys = pg < max_pages ? block_row[pg] : -1;
+        if (phys < -1) {
+            free(hot_row); free(res_row);
+            return ORC_EPRECOND;
+        }
+        if (phys >= 0) {
+            res_row[i] = (int64_t)phys * page_size + t % page_size;
+            hot_row[i] = -1;                 /* leaves the hot tiers untouched */
+        }
+    }
+    /* The remaining entries go through the hot tiers as usual. */
+    rc = orc_swap_in_row(B, K, rb, max_seq, L, 0, hot_row, out, lru, tok, host_req, hot_req,
+                         plan_pos, plan_slot, plan_count);
+    if (rc == ORC_OK) {
+        for (int32_t i = 0; i < K; ++i) {
+            int64_t v;
+            if (res_row[i] >= 0)
+                v = res_row[i];
+            else if (out[i] < 0)
+                v = -1;
+            else
+                v = hot_base + out[i];
+            if (v > INT32_MAX) {
+                rc = ORC_EPRECOND;
+                break;
+            }
+            out[i] = (int32_t)v;
+        }
+    }
+    free(hot_row); free(res_row);
+    return rc;
+}
+
+int orc_swap_in_paged(int32_t R, int32_t B, int32_t K, int64_t rb, int32_t max_seq,
+                      int32_t nb, const int32_t* req_idx,
+                      const int32_t* topk, const int32_t* seq_lens,
+                      const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                      int64_t hot_row_base, int32_t* out,
+                      int32_t* lru, int32_t* tok,
+                      const uint8_t* host, uint8_t* hot,
+                      int32_t* plan_pos, int32_t* plan_slot, int32_t* plan_count)
+{
+    if (R <= 0 || nb < 0 || nb > R)
+        return ORC_EINVAL;
+    for (int32_t b = 0; b < nb; ++b) {
+        int32_t r = req_idx ? req_idx[b] : b;
+        if (r < 0 || r >= R)
+            return ORC_EINVAL;
+        int rc = orc_swap_in_row_paged(
+            B, K, rb, max_seq, seq_lens[b],
+            block_table ? block_table + (int64_t)b * max_pages : NULL, max_pages, page_size,
+            hot_row_base + (int64_t)r * (B + 1),
             topk + (int64_t)b * K, out + (int64_t)b * K,
             lru + (int64_t)r * B, tok + (int64_t)r * B,
             host + (int64_t)r * max_seq * rb, hot + (int64_t)r * (B + 1) * rb,

@@ -69,6 +69,27 @@ int orc_swap_in(int32_t R, int32_t B, int32_t K, int64_t rb, int32_t max_seq,
                 const uint8_t* host, uint8_t* hot,
                 int32_t* plan_pos, int32_t* plan_slot, int32_t* plan_count);
 
+/* Per-page residency: block_row[p] = physical page of page p (-1 = host
+ * backed); outputs are physical rows in the caller's view (resident rows
+ * block_row[t/P]*P + t%P, hot rows hot_base + slot). */
+int orc_swap_in_row_paged(int32_t B, int32_t K, int64_t rb, int32_t max_seq,
+                          int32_t L, const int32_t* block_row, int32_t max_pages,
+                          int32_t page_size, int64_t hot_base,
+                          const int32_t* topk, int32_t* out,
+                          int32_t* lru, int32_t* tok,
+                          const uint8_t* host_req, uint8_t* hot_req,
+                          int32_t* plan_pos, int32_t* plan_slot, int32_t* plan_count);
+
+/* Batched form; request r's hot rows start at hot_row_base + r*(B+1). */
+int orc_swap_in_paged(int32_t R, int32_t B, int32_t K, int64_t rb, int32_t max_seq,
+                      int32_t nb, const int32_t* req_idx,
+                      const int32_t* topk, const int32_t* seq_lens,
+                      const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                      int64_t hot_row_base, int32_t* out,
+                      int32_t* lru, int32_t* tok,
+                      const uint8_t* host, uint8_t* hot,
+                      int32_t* plan_pos, int32_t* plan_slot, int32_t* plan_count);
+
 /* Skip layer: repeat the anchor's recorded misses on another layer's pool. */
 int orc_replay(int32_t R, int32_t B, int32_t K, int64_t rb, int32_t max_seq,
                int32_t nb, const int32_t* req_idx,

@@ -66,11 +66,13 @@ def load_oracle(path: str = LIB) -> ctypes.CDLL:
                                     _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.orc_swap_in.argtypes = [_I32, _I32, _I32, _I64, _I32, _I32, _P,
                                 _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.orc_swap_in_paged.argtypes = [_I32, _I32, _I32, _I64, _I32, _I32, _P,
+                                      _P, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.orc_replay.argtypes = [_I32, _I32, _I32, _I64, _I32, _I32, _P,
                                _P, _P, _P, _P, _P]
     lib.orc_backup.argtypes = [_I32, _I32, _I64, _I32, _I32, _P, _P, _P, _P, _P]
     for fn in ("orc_admit_state", "orc_admit_fill", "orc_store_newest",
-               "orc_swap_in_row", "orc_swap_in", "orc_replay", "orc_backup"):
+               "orc_swap_in_row", "orc_swap_in", "orc_swap_in_paged", "orc_replay", "orc_backup"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -184,6 +186,29 @@ class Oracle:
             _ptr(self.host[anchor]), _ptr(self.hot[anchor]),
             _ptr(plan.pos), _ptr(plan.slot), _ptr(plan.count))
         self._check(rc, "swap_in")
+        return out, plan
+
+    def swap_in_paged(self, anchor: int, topk, seq_lens, block_table, page_size: int,
+                      hot_row_base: int = 0, req_idx=None):
+        """Per-page residency: block_table [nb][max_pages] int32 (physical page
+        or -1 for a host-backed page).  Returns physical rows in the caller's
+        view: resident rows page*P + t%P, hot rows hot_row_base + r*(B+1) + slot."""
+        topk = _i32(topk)
+        seq_lens = _i32(seq_lens)
+        nb = topk.shape[0]
+        bt = _i32(block_table) if block_table is not None else None
+        max_pages = 0 if bt is None else int(bt.shape[1])
+        ridx = _i32(req_idx) if req_idx is not None else None
+        out = np.empty((nb, self.K), np.int32)
+        plan = Plan(np.full((nb, self.K), -7, np.int32), np.full((nb, self.K), -7, np.int32),
+                    np.zeros(nb, np.int32))
+        rc = self.lib.orc_swap_in_paged(
+            self.R, self.B, self.K, self.rb, self.max_seq, nb, _ptr(ridx),
+            _ptr(topk), _ptr(seq_lens), _ptr(bt), max_pages, int(page_size), int(hot_row_base), _ptr(out),
+            _ptr(self.lru[anchor]), _ptr(self.tok[anchor]),
+            _ptr(self.host[anchor]), _ptr(self.hot[anchor]),
+            _ptr(plan.pos), _ptr(plan.slot), _ptr(plan.count))
+        self._check(rc, "swap_in_paged")
         return out, plan
 
     def replay(self, skip_layer: int, plan: Plan, req_idx=None):

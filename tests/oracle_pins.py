@@ -21,6 +21,11 @@ What each pin rests on:
   * pin_hand_trace: a trace worked out by hand (tests/golden).
   * pin_replay: a skip layer that replays the plan ends up byte-identical to
     one resolved directly (SGLang guide, "Shared-index prefetch").
+  * pin_paged_*: per-page residency (vLLM design note, "Resident device
+    pages"): a hand-worked trace; every page resident gives page*P + t%P
+    and moves nothing; no page resident gives the per-request resolver's
+    result; and in the caller's combined row view every resolved row holds
+    the position's KV while resident positions never reach the hot tiers.
 """
 from __future__ import annotations
 
@@ -357,6 +362,157 @@ def pin_preconditions(lib) -> List[str]:
     return fails
 
 
+# ---------------------------------------------------------------------------
+# per-page residency
+# ---------------------------------------------------------------------------
+def pin_paged_hand_trace(lib) -> List[str]:
+    with open(os.path.join(GOLDEN, "hand_worked_trace.json")) as f:
+        g = json.load(f)
+    fails = []
+    for tr in g["paged_traces"]:
+        B, K, L0, P = tr["B"], tr["K"], tr["L0"], tr["page_size"]
+        orc = _tiny_oracle(lib, 1, B, K, L0 + len(tr["steps"]) + 1)
+        _fill_host(orc, [L0])
+        orc.admit(0, [0], [L0])
+        bt = np.array([tr["block_row"]], np.int32)
+        for k, st in enumerate(tr["steps"]):
+            L = np.array([st["L"]], np.int32)
+            orc.store_newest(0, _new_kv(1, L), L)
+            out, plan = orc.swap_in_paged(0, np.array([st["topk"]], np.int32), L, bt, P, tr["hot_base"])
+            orc.backup(0, L)
+            got = dict(out=out[0].tolist(), lru=orc.lru[0][0].tolist(), tok=orc.tok[0][0].tolist(),
+                       plan_pos=plan.pos[0, : plan.count[0]].tolist(),
+                       plan_slot=plan.slot[0, : plan.count[0]].tolist())
+            for key in got:
+                if got[key] != st[key]:
+                    fails.append(f"paged hand trace step {k}: {key} {got[key]} != {st[key]}")
+    return fails
+
+
+def _paged_setup(lib, R, B, K, P, L0, steps, frac, seed, n_phys_extra=7):
+    """A cache, a block table with a seeded share `frac` of resident pages
+    (distinct physical pages in a shuffled order), and a resident cache
+    [n_phys*P][RB] holding the same KV as the host pool for resident pages."""
+    rng = np.random.default_rng(seed)
+    max_seq = int(L0.max()) + steps + 1
+    max_pages = (max_seq + P - 1) // P
+    orc = _tiny_oracle(lib, R, B, K, max_seq)
+    _fill_host(orc, L0)
+    orc.admit(0, np.arange(R), L0)
+    n_res = int(round(frac * R * max_pages))
+    flat = np.full(R * max_pages, -1, np.int32)
+    chosen = rng.choice(R * max_pages, size=n_res, replace=False)
+    n_phys = n_res + n_phys_extra
+    flat[chosen] = rng.choice(n_phys, size=n_res, replace=False)
+    bt = flat.reshape(R, max_pages)
+    res_cache = np.zeros((n_phys * P, RB), np.uint8)
+    for r in range(R):
+        for pg in range(max_pages):
+            if bt[r, pg] >= 0:
+                for off in range(P):
+                    t = pg * P + off
+                    if t < max_seq:
+                        res_cache[bt[r, pg] * P + off] = orc.host[0][r, t]
+    return orc, bt, res_cache, rng, max_seq
+
+
+def pin_paged_closed_forms(lib) -> List[str]:
+    fails = []
+    R, B, K, P = 3, 16, 6, 4
+    L0 = np.array([10, 30, 60], np.int32)
+    # every page resident: tier 0 answers everything, nothing else moves
+    orc, _, _, rng, max_seq = _paged_setup(lib, R, B, K, P, L0, 3, 0.0, 1)
+    max_pages = (max_seq + P - 1) // P
+    bt = np.arange(R * max_pages, dtype=np.int32)[::-1].copy().reshape(R, max_pages)
+    for k in range(3):
+        L = L0 + 1 + k
+        topk = np.stack([rng.choice(int(L[r]), K, replace=False) for r in range(R)]).astype(np.int32)
+        lru0, tok0, hot0 = orc.lru[0].copy(), orc.tok[0].copy(), orc.hot[0].copy()
+        out, plan = orc.swap_in_paged(0, topk, L, bt, P, 1000)
+        exp = bt[np.arange(R)[:, None], topk // P] * P + topk % P
+        if not np.array_equal(out, exp):
+            fails.append(f"paged closed form: all-resident step {k}: out != page*P + t%P")
+        if plan.count.any() or not np.array_equal(orc.lru[0], lru0) or not np.array_equal(orc.tok[0], tok0) \
+                or not np.array_equal(orc.hot[0], hot0):
+            fails.append(f"paged closed form: all-resident step {k}: state, plan or bytes changed")
+    # no page resident: the per-request resolver, shifted into the caller's row view
+    a, _, _, rng, _ = _paged_setup(lib, R, B, K, P, L0, 5, 0.0, 2)
+    b, _, _, _, _ = _paged_setup(lib, R, B, K, P, L0, 5, 0.0, 2)
+    base = 77
+    for k in range(5):
+        L = L0 + 1 + k
+        topk = np.stack([rng.choice(int(L[r]), K, replace=False) for r in range(R)]).astype(np.int32)
+        for o in (a, b):
+            o.store_newest(0, _new_kv(R, L), L)
+        oa, pa = a.swap_in_paged(0, topk, L, None, P, base)
+        ob, pb = b.swap_in(0, topk, L)
+        exp = np.where(ob >= 0, base + np.arange(R)[:, None] * (B + 1) + ob, -1)
+        if not np.array_equal(oa, exp) or not np.array_equal(pa.count, pb.count):
+            fails.append(f"paged closed form: no-resident step {k}: differs from the per-request resolver")
+        if not (np.array_equal(a.lru[0], b.lru[0]) and np.array_equal(a.tok[0], b.tok[0])):
+            fails.append(f"paged closed form: no-resident step {k}: state differs")
+        for o in (a, b):
+            o.backup(0, L)
+    return fails
+
+
+def pin_paged_bytes(lib, steps: int = 10) -> List[str]:
+    """The pages' correctness statement in the caller's combined row view
+    (resident cache rows, then the hot rows): every resolved row holds the KV
+    of the position asked for; resident positions never enter the slot map or
+    the plan."""
+    fails = []
+    R, B, K, P = 5, 24, 10, 4
+    L0 = np.array([15, 24, 40, 90, 200], np.int32)
+    for frac in (0.2, 0.5, 0.8):
+        orc, bt, res_cache, rng, max_seq = _paged_setup(lib, R, B, K, P, L0, steps, frac, 7)
+        base = res_cache.shape[0]
+        for k in range(steps):
+            L = L0 + 1 + k
+            topk = np.full((R, K), -1, np.int32)
+            for r in range(R):
+                n = min(K, int(L[r]))
+                hi = int(L[r])
+                lo = max(0, hi - 3 * K)
+                topk[r, :n] = rng.choice(np.arange(lo, hi), n, replace=False) if hi - lo >= n else \
+                    rng.choice(hi, n, replace=False)
+            nk = _new_kv(R, L)
+            orc.store_newest(0, nk, L)
+            for r in range(R):          # the forward also writes a resident newest page
+                pg = (int(L[r]) - 1) // P
+                if bt[r, pg] >= 0:
+                    res_cache[bt[r, pg] * P + (int(L[r]) - 1) % P] = nk[r]
+            tok0 = orc.tok[0].copy()
+            out, plan = orc.swap_in_paged(0, topk, L, bt, P, base)
+            view = np.concatenate([res_cache, orc.hot[0].reshape(R * (B + 1), RB)])
+            for r in range(R):
+                for i in range(K):
+                    t = int(topk[r, i])
+                    if t < 0:
+                        if out[r, i] != -1:
+                            fails.append("paged bytes: padding not -1")
+                        continue
+                    want = nk[r] if t == L[r] - 1 else orc.host[0][r, t]
+                    if not (0 <= out[r, i] < view.shape[0]) or not np.array_equal(view[out[r, i]], want):
+                        fails.append(f"paged bytes frac {frac} step {k} r {r} i {i}: row {out[r, i]} "
+                                     f"does not hold position {t}")
+                        break
+                    resident = bt[r, t // P] >= 0
+                    if resident != (out[r, i] < base):
+                        fails.append(f"paged bytes: position {t} resolved in the wrong tier")
+                        break
+                c = int(plan.count[r])
+                if any(bt[r, int(t) // P] >= 0 for t in plan.pos[r, :c]):
+                    fails.append(f"paged bytes: a resident position was copied")
+                changed = orc.tok[0][r][orc.tok[0][r] != tok0[r]]
+                if any(bt[r, int(t) // P] >= 0 for t in changed):
+                    fails.append(f"paged bytes: a resident position entered the slot map")
+            orc.backup(0, L)
+            if len(fails) > 5:
+                return fails
+    return fails
+
+
 # cheapest first: a planted mistake is usually caught within milliseconds
 ALL_PINS = {
     "hand_trace": pin_hand_trace,
@@ -364,6 +520,9 @@ ALL_PINS = {
     "invariants": pin_invariants,
     "replay": pin_replay,
     "preconditions": pin_preconditions,
+    "paged_hand_trace": pin_paged_hand_trace,
+    "paged_closed_forms": pin_paged_closed_forms,
+    "paged_bytes": pin_paged_bytes,
     "textbook_lru_random": pin_textbook_lru_random,
     "textbook_lru_exhaustive": pin_textbook_lru_exhaustive,
 }

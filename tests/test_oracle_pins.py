@@ -63,6 +63,16 @@ MUTANTS = [
     ("padding resolved as position", "            out[i] = -1;                    /* padding */",
      "            out[i] = t + 1;                 /* padding */"),
     ("duplicate top-k accepted", "if (t < -1 || t >= L || seen[t]) {", "if (t < -1 || t >= L) {"),
+    ("resident row: page and offset swapped", "res_row[i] = (int64_t)phys * page_size + t % page_size;",
+     "res_row[i] = (int64_t)(t % page_size) * page_size + phys;"),
+    ("resident entry left in the hot tiers", "hot_row[i] = -1;                 /* leaves the hot tiers untouched */",
+     "(void)0;"),
+    ("hot rows not shifted into the caller's view", "v = hot_base + out[i];", "v = out[i];"),
+    ("page looked up by offset", "int32_t pg = t / page_size;", "int32_t pg = t % page_size;"),
+    ("page past the table taken as resident", "int32_t phys = pg < max_pages ? block_row[pg] : -1;",
+     "int32_t phys = pg < max_pages ? block_row[pg] : 0;"),
+    ("physical page 0 not resident", "if (phys >= 0) {\n            res_row", "if (phys > 0) {\n            res_row"),
+    ("hot base of request 0 used for all", "hot_row_base + (int64_t)r * (B + 1),", "hot_row_base,"),
 ]
 
 
