@@ -178,7 +178,8 @@ def main():
         main = torch.cuda.current_stream(dev)
         if timed:
             # events bracket each swap-in on the stream it is launched on
-            orig = g.cache.swap_in
+            name = "swap_in_paged" if g.paged else "swap_in"
+            orig = getattr(g.cache, name)
 
             def timed_swap_in(*a, **kw):
                 e0 = torch.cuda.Event(enable_timing=True)
@@ -187,11 +188,11 @@ def main():
                 orig(*a, **kw)
                 e1.record(main)
                 ev.append((e0, e1))
-            g.cache.swap_in = timed_swap_in
+            setattr(g.cache, name, timed_swap_in)
             try:
                 g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=between)
             finally:
-                g.cache.swap_in = orig
+                setattr(g.cache, name, orig)
         else:
             g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=between)
 
@@ -250,6 +251,7 @@ def main():
             "workload": wl.name, "requests": wl.R, "layers": wl.num_layers, "anchors": len(wl.anchors),
             "top_k": wl.K, "device_buffer_size": wl.B, "row_bytes": wl.rb, "verify_rows": wl.spec,
             "resident_requests": wl.n_resident, "first_seq_len": list(wl.seq_first),
+            "page_size": wl.page_size or None, "resident_page_frac": wl.resident_page_frac if wl.page_size else None,
             "parallelism": "single GPU (requests are independent)",
             "prefetch": bool(g.prefetch) if wl.skip_layers else None,
             "layer_compute_mib": args.layer_compute_mib,

@@ -193,9 +193,32 @@ struct SwapInArgs {
     uint8_t* hot;                // [R][B+1][rb]
     uint32_t* err;
     int32_t R, B, K, rb, max_seq, hash_bits;
+    // per-page residency (paged != 0): block_table [nb][max_pages] physical
+    // page or -1; outputs are rows of the caller's view (resident rows
+    // page * page_size + t % page_size, hot rows hot_row_base + r*(B+1) + slot)
+    const int32_t* block_table;
+    int32_t paged, max_pages, page_size, hot_row_base;
 };
 
 constexpr unsigned long long kHashEmpty = ~0ull;
+constexpr uint32_t kResidentIdx = 0x80000000u;   // hash value flag: the entry resolved in tier 0
+
+// Tier 0 of the paged resolver: the physical row of position t (0 <= t) when
+// its page is resident, else -1; a bad block-table entry sets *err.
+__device__ __forceinline__ int resident_row(const int32_t* bt_row, int max_pages, int page_size, int t,
+                                            uint32_t* err)
+{
+    const int pg = t / page_size;
+    if (pg >= max_pages) return -1;          // past the table: host-backed
+    const int phys = bt_row[pg];
+    if (phys < 0) {
+        if (phys < -1) *err |= HISPARSE_DERR_PAGE;
+        return -1;
+    }
+    const long long row = static_cast<long long>(phys) * page_size + t % page_size;
+    if (row > INT_MAX) { *err |= HISPARSE_DERR_PAGE; return -1; }
+    return static_cast<int>(row);
+}
 
 struct SwapInLds {
     unsigned long long* hash;  // [1 << hash_bits]  (position << 32) | top-k index; kHashEmpty = free
@@ -252,13 +275,35 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
 
     // Tier 0 (resident request) and the short-sequence fast path: the slot
     // is the position; no state, no plan, no copy.
-    if ((a.resident && a.resident[b]) || L <= B) {
+    if (!a.paged && ((a.resident && a.resident[b]) || L <= B)) {
         for (int i = tid; i < K; i += nthr) out[i] = topk[i];
         if (tid == 0) a.plan_count[b] = 0;
         return;
     }
     const int r = a.req_idx ? a.req_idx[b] : b;
     if (r < 0 || r >= a.R) { fail_row(a, b, HISPARSE_DERR_REQ_IDX); return; }
+    const int32_t* bt_row = a.paged ? a.block_table + size_t(b) * a.max_pages : nullptr;
+    const int hot_base = a.paged ? a.hot_row_base + r * (B + 1) : 0;
+    if (a.paged && L <= B) {
+        // Paged fast path: resident pages resolve in tier 0, every other
+        // position sits at slot = position.  Checked first, written second,
+        // so a bad row changes nothing.
+        uint32_t perr = 0;
+        for (int i = tid; i < K; i += nthr) {
+            const int t = topk[i];
+            if (t < -1 || t >= L) perr |= HISPARSE_DERR_TOPK_RANGE;
+            else if (t >= 0) (void)resident_row(bt_row, a.max_pages, a.page_size, t, &perr);
+        }
+        if (__syncthreads_or(perr != 0)) { fail_row(a, b, perr); return; }
+        for (int i = tid; i < K; i += nthr) {
+            const int t = topk[i];
+            uint32_t unused = 0;
+            const int rr = t >= 0 ? resident_row(bt_row, a.max_pages, a.page_size, t, &unused) : -1;
+            out[i] = t < 0 ? -1 : (rr >= 0 ? rr : hot_base + t);
+        }
+        if (tid == 0) a.plan_count[b] = 0;
+        return;
+    }
     if (L > a.max_seq) { fail_row(a, b, HISPARSE_DERR_SEQ_LEN); return; }
 
     SwapInLds s = carve_lds(smem, B, K, a.hash_bits);
@@ -292,6 +337,7 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
 
     // -- classify the top-k row ------------------------------------------
     uint32_t err = 0;
+    uint32_t rbits = 0;                            // entries resolved in tier 0 (resident page)
 #pragma unroll
     for (int k = 0; k < EK; ++k) {
         const int c = k * nwaves + wave, i = c * kWave + lane;
@@ -300,8 +346,12 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
             int cls;
             if (t == -1) cls = -1;
             else if (t < -1 || t >= L) { cls = -1; err |= HISPARSE_DERR_TOPK_RANGE; }
-            else if (t == L - 1) cls = B;          // newest token: its own row
-            else cls = kMissMark;
+            else {
+                const int rr = a.paged ? resident_row(bt_row, a.max_pages, a.page_size, t, &err) : -1;
+                if (rr >= 0) { cls = rr; rbits |= 1u << k; }   // resident page: physical row
+                else if (t == L - 1) cls = B;                 // newest token: its own row
+                else cls = kMissMark;
+            }
             s.out_s[i] = cls;
         }
     }
@@ -312,9 +362,12 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
     for (int k = 0; k < EK; ++k) {
         const int c = k * nwaves + wave, i = c * kWave + lane;
         const int t = t_own[k];
-        if (c < nck && i < K && t >= 0 && t < L - 1) {
+        const bool res = (rbits >> k) & 1u;
+        // resident entries go in too (flagged), so a repeated position is
+        // caught whatever its tier and a slot holding it is never a hit
+        if (c < nck && i < K && t >= 0 && t < L && (res || t < L - 1)) {
             const unsigned long long e = (static_cast<unsigned long long>(static_cast<uint32_t>(t)) << 32) |
-                                         static_cast<uint32_t>(i);
+                                         (static_cast<uint32_t>(i) | (res ? kResidentIdx : 0u));
             uint32_t h = hash_slot(t, a.hash_bits);
             for (;;) {   // the table has at least 4K entries, so a free one is always reached
                 const unsigned long long prev = atomicCAS(&s.hash[h], kHashEmpty, e);
@@ -366,9 +419,12 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
                     pending &= ~(1u << q);
                 } else if (static_cast<uint32_t>(e >> 32) == static_cast<uint32_t>(tok_own[k])) {
                     const int x = (k * nwaves + wave) * kWave + lane;
-                    const int i = static_cast<int>(static_cast<uint32_t>(e));
-                    if (atomicCAS(&s.out_s[i], kMissMark, x) == kMissMark) s.hit[x] = 1;
-                    else err |= HISPARSE_DERR_STATE;   // two slots claim one position
+                    const uint32_t v = static_cast<uint32_t>(e);
+                    if (!(v & kResidentIdx)) {        // a resident position is never a hot hit
+                        const int i = static_cast<int>(v);
+                        if (atomicCAS(&s.out_s[i], kMissMark, x) == kMissMark) s.hit[x] = 1;
+                        else err |= HISPARSE_DERR_STATE;   // two slots claim one position
+                    }
                     pending &= ~(1u << q);
                 } else {
                     h[q] = (h[q] + 1) & hmask;
@@ -476,7 +532,10 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
 #pragma unroll
     for (int k = 0; k < EK; ++k) {
         const int c = k * nwaves + wave, i = c * kWave + lane;
-        if (c < nck && i < K) out[i] = m_own[k] >= 0 ? s.plan_v[m_own[k]] : s.out_s[i];
+        if (c < nck && i < K) {
+            const int o = m_own[k] >= 0 ? s.plan_v[m_own[k]] : s.out_s[i];
+            out[i] = ((rbits >> k) & 1u) || o < 0 ? o : hot_base + o;   // hot rows into the caller's view
+        }
     }
     int32_t* pp = a.plan_pos + size_t(b) * K;
     int32_t* ps = a.plan_slot + size_t(b) * K;
@@ -962,23 +1021,51 @@ int hisparse_store_newest(hisparse_ctx* c, int32_t layer, const void* new_rows, 
     return hip_rc(hipGetLastError());
 }
 
+namespace {
+
+int launch_swap_in(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_idx, const int32_t* seq_lens,
+                   const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb, int32_t* out,
+                   hisparse_plan plan_row, const int32_t* block_table, int32_t paged, int32_t max_pages,
+                   int32_t page_size, int32_t hot_row_base, hipStream_t stream)
+{
+    if (!c || !is_anchor(c, anchor_layer) || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
+    if (nb == 0) return HISPARSE_OK;
+    if (!topk_idx || !seq_lens || !out || !plan_row.pos || !plan_row.slot || !plan_row.count)
+        return HISPARSE_EINVAL;
+    SwapInArgs a{};
+    a.topk = topk_idx; a.seq_lens = seq_lens; a.resident = resident_mask; a.req_idx = req_idx;
+    a.out = out; a.plan_pos = plan_row.pos; a.plan_slot = plan_row.slot; a.plan_count = plan_row.count;
+    a.lru = c->lru[anchor_layer]; a.tok = c->tok[anchor_layer];
+    a.host = c->host[anchor_layer]; a.hot = c->hot[anchor_layer]; a.err = c->err;
+    a.R = c->R; a.B = c->B; a.K = c->K; a.rb = c->rb; a.max_seq = c->max_seq; a.hash_bits = c->hash_bits;
+    a.block_table = block_table; a.paged = paged; a.max_pages = max_pages; a.page_size = page_size;
+    a.hot_row_base = hot_row_base;
+    void* args[] = {&a};
+    return hip_rc(hipLaunchKernel(reinterpret_cast<const void*>(c->swap_in_fn), dim3(nb), dim3(c->block), args,
+                                  c->lds, stream));
+}
+
+}  // namespace
+
 int hisparse_swap_in(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_idx, const int32_t* seq_lens,
                      const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb, int32_t* out_slots,
                      hisparse_plan plan_row, hipStream_t stream)
 {
-    if (!c || !is_anchor(c, anchor_layer) || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
-    if (nb == 0) return HISPARSE_OK;
-    if (!topk_idx || !seq_lens || !out_slots || !plan_row.pos || !plan_row.slot || !plan_row.count)
+    return launch_swap_in(c, anchor_layer, topk_idx, seq_lens, resident_mask, req_idx, nb, out_slots, plan_row,
+                          nullptr, 0, 0, 1, 0, stream);
+}
+
+int hisparse_swap_in_paged(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_idx, const int32_t* seq_lens,
+                           const int32_t* block_table, int32_t max_pages, int32_t page_size, int32_t hot_row_base,
+                           const int32_t* req_idx, int32_t nb, int32_t* out_rows, hisparse_plan plan_row,
+                           hipStream_t stream)
+{
+    if (!c || page_size < 1 || max_pages < 0 || (max_pages > 0 && !block_table) || hot_row_base < 0)
         return HISPARSE_EINVAL;
-    SwapInArgs a{};
-    a.topk = topk_idx; a.seq_lens = seq_lens; a.resident = resident_mask; a.req_idx = req_idx;
-    a.out = out_slots; a.plan_pos = plan_row.pos; a.plan_slot = plan_row.slot; a.plan_count = plan_row.count;
-    a.lru = c->lru[anchor_layer]; a.tok = c->tok[anchor_layer];
-    a.host = c->host[anchor_layer]; a.hot = c->hot[anchor_layer]; a.err = c->err;
-    a.R = c->R; a.B = c->B; a.K = c->K; a.rb = c->rb; a.max_seq = c->max_seq; a.hash_bits = c->hash_bits;
-    void* args[] = {&a};
-    return hip_rc(hipLaunchKernel(reinterpret_cast<const void*>(c->swap_in_fn), dim3(nb), dim3(c->block), args,
-                                  c->lds, stream));
+    if (static_cast<long long>(hot_row_base) + static_cast<long long>(c->R) * (c->B + 1) > INT_MAX)
+        return HISPARSE_EINVAL;
+    return launch_swap_in(c, anchor_layer, topk_idx, seq_lens, nullptr, req_idx, nb, out_rows, plan_row,
+                          block_table, 1, max_pages, page_size, hot_row_base, stream);
 }
 
 int hisparse_replay_plan(hisparse_ctx* c, int32_t skip_layer, hisparse_plan plan_row, const int32_t* req_idx,

@@ -27,6 +27,7 @@ HISPARSE_DERR_SEQ_LEN = 0x4
 HISPARSE_DERR_REQ_IDX = 0x8
 HISPARSE_DERR_STATE = 0x10
 HISPARSE_DERR_PLAN = 0x20
+HISPARSE_DERR_PAGE = 0x40
 
 HISPARSE_HOST_DEFAULT = 0
 HISPARSE_HOST_COHERENT = 1
@@ -35,7 +36,7 @@ HISPARSE_HOST_NONCOHERENT = 2
 # every entry point include/hisparse.h declares
 EXPORTS = (
     "hisparse_init", "hisparse_destroy", "hisparse_admit", "hisparse_store_newest",
-    "hisparse_swap_in", "hisparse_replay_plan", "hisparse_backup", "hisparse_get_state",
+    "hisparse_swap_in", "hisparse_swap_in_paged", "hisparse_replay_plan", "hisparse_backup", "hisparse_get_state",
     "hisparse_set_state", "hisparse_get_error", "hisparse_host_alloc", "hisparse_host_free",
     "hisparse_swap_in_lds_bytes", "hisparse_strerror", "hisparse_version",
 )
@@ -90,6 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hisparse_admit.argtypes = [P, I32, P, P, I32, P]
     lib.hisparse_store_newest.argtypes = [P, I32, P, P, P, P, I32, P]
     lib.hisparse_swap_in.argtypes = [P, I32, P, P, P, P, I32, P, hisparse_plan, P]
+    lib.hisparse_swap_in_paged.argtypes = [P, I32, P, P, P, I32, I32, I32, P, I32, P, hisparse_plan, P]
     lib.hisparse_replay_plan.argtypes = [P, I32, hisparse_plan, P, I32, P]
     lib.hisparse_backup.argtypes = [P, I32, P, P, P, I32, P]
     lib.hisparse_get_state.argtypes = [P, I32, P, P, P]
@@ -202,6 +204,15 @@ def hisparse_swap_in(ctx: int, anchor_layer: int, topk_idx, seq_lens, resident_m
                                    _stream(stream)), "hisparse_swap_in")
 
 
+def hisparse_swap_in_paged(ctx: int, anchor_layer: int, topk_idx, seq_lens, block_table, page_size: int,
+                           hot_row_base: int, req_idx, out_rows, plan: Plan, stream=None) -> None:
+    max_pages = 0 if block_table is None else int(block_table.shape[1])
+    _check(_lib().hisparse_swap_in_paged(ctx, anchor_layer, _ptr(topk_idx), _ptr(seq_lens), _ptr(block_table),
+                                         max_pages, page_size, hot_row_base, _ptr(req_idx),
+                                         int(topk_idx.shape[0]), _ptr(out_rows), plan.c(), _stream(stream)),
+           "hisparse_swap_in_paged")
+
+
 def hisparse_replay_plan(ctx: int, skip_layer: int, plan: Plan, req_idx=None, stream=None) -> None:
     _check(_lib().hisparse_replay_plan(ctx, skip_layer, plan.c(), _ptr(req_idx), int(plan.count.shape[0]),
                                        _stream(stream)), "hisparse_replay_plan")
@@ -300,6 +311,11 @@ class HiSparseCache:
 
     def swap_in(self, anchor, topk_idx, seq_lens, resident_mask, req_idx, out_slots, plan, stream=None):
         hisparse_swap_in(self.ctx, anchor, topk_idx, seq_lens, resident_mask, req_idx, out_slots, plan, stream)
+
+    def swap_in_paged(self, anchor, topk_idx, seq_lens, block_table, page_size, hot_row_base, req_idx, out_rows,
+                      plan, stream=None):
+        hisparse_swap_in_paged(self.ctx, anchor, topk_idx, seq_lens, block_table, page_size, hot_row_base,
+                               req_idx, out_rows, plan, stream)
 
     def replay_plan(self, skip_layer, plan, req_idx=None, stream=None):
         hisparse_replay_plan(self.ctx, skip_layer, plan, req_idx, stream)

@@ -56,6 +56,18 @@ class GpuRun:
         self.plans = {g: [Plan.empty(wl.R, wl.K, self.dev) for _ in range(wl.spec)] for g in wl.anchors}
         self.side = torch.cuda.Stream(device=self.dev)
         self.events: Dict[int, "torch.cuda.Event"] = {}
+        # per-page residency: the block table, and per layer a resident cache
+        # [n_phys * P][rb] holding the resident pages' KV; the caller's row
+        # view is the resident cache's rows, then the hot buffer's rows.
+        self.paged = wl.page_size > 0
+        if self.paged:
+            assert wl.n_resident == 0, "per-page residency replaces the per-request mask"
+            bt, n_phys = W.block_table(wl, self.steps)
+            self.block_table_np = bt
+            self.block_table = torch.from_numpy(bt).to(self.dev)
+            self.hot_row_base = n_phys * wl.page_size
+            self.res_cache = [torch.zeros(n_phys * wl.page_size, wl.rb, dtype=torch.uint8, device=self.dev)
+                              for _ in range(wl.num_layers)]
         if fill:
             self.fill_and_admit()
 
@@ -64,33 +76,74 @@ class GpuRun:
         torch, wl = self.torch, self.wl
         for l in range(wl.num_layers):
             W.fill_host_pool(self.cache.host[l], wl, l, self.L0, self.dev)
+        if self.paged:
+            self._fill_resident()
         req = torch.arange(wl.R, dtype=torch.int32, device=self.dev)
         L0 = torch.from_numpy(self.L0.astype(np.int32)).to(self.dev)
         for g in wl.anchors:
             self.cache.admit(g, req, L0)
         torch.cuda.synchronize(self.dev)
 
+    def _fill_resident(self):
+        """Resident pages hold the same KV as the host pool (prefill's rows)."""
+        torch, wl, P = self.torch, self.wl, self.wl.page_size
+        r_idx, p_idx = np.nonzero(self.block_table_np >= 0)
+        phys = self.block_table_np[r_idx, p_idx]
+        for l in range(wl.num_layers):
+            host = self.cache.host[l]
+            for r, pg, ph in zip(r_idx.tolist(), p_idx.tolist(), phys.tolist()):
+                lo, hi = pg * P, min((pg + 1) * P, self.max_seq)
+                self.res_cache[l][ph * P: ph * P + (hi - lo)].copy_(host[r, lo:hi], non_blocking=False)
+
+    def store_newest_resident(self, layer: int, new_kv_l, seq_lens_np):
+        """The forward's KV write for requests whose newest page is resident."""
+        P = self.wl.page_size
+        pg = (seq_lens_np - 1) // P
+        rows = []
+        for r in range(self.wl.R):
+            ph = self.block_table_np[r, pg[r]] if pg[r] < self.block_table_np.shape[1] else -1
+            if ph >= 0:
+                rows.append((r, ph * P + (seq_lens_np[r] - 1) % P))
+        if rows:
+            src = self.torch.tensor([int(r) for r, _ in rows], dtype=self.torch.long, device=self.dev)
+            dst = self.torch.tensor([int(d) for _, d in rows], dtype=self.torch.long, device=self.dev)
+            self.res_cache[layer].index_copy_(0, dst, new_kv_l.index_select(0, src))
+
+    def row_view(self, layer: int):
+        """The caller's row view of one layer: resident cache rows, then hot rows."""
+        wl = self.wl
+        return self.torch.cat([self.res_cache[layer], self.cache.hot[layer].view(wl.R * (wl.B + 1), wl.rb)])
+
     def seq_lens(self, step: int):
         return self.torch.from_numpy(W.seq_lens_at(self.wl, step).astype(np.int32)).to(self.dev)
 
     # -- one decode step ------------------------------------------------------
     def step(self, topk: Dict[int, "torch.Tensor"], new_kv: "torch.Tensor", seq_lens,
-             between_layers=None, after_swap_in=None, plans: Optional[Dict[int, List[Plan]]] = None):
+             between_layers=None, after_swap_in=None, plans: Optional[Dict[int, List[Plan]]] = None,
+             seq_lens_np=None):
         """topk[g]: [S][R][K] int32 (device) for every anchor g; new_kv:
         [layers][R][rb] uint8 (device); seq_lens: [R] int32 (device).
         between_layers(l) runs on the main stream after layer l (a stand-in for
         the layer's other compute); after_swap_in(g, s) runs right after each
         swap-in (the consumer of that verify row); plans replaces the plan rows
-        this step records into (default: self.plans)."""
+        this step records into (default: self.plans); seq_lens_np (host copy
+        of seq_lens) lets a paged run write the newest token into a resident
+        page, as the forward would."""
         torch, wl, c = self.torch, self.wl, self.cache
         plans = self.plans if plans is None else plans
         main = torch.cuda.current_stream(self.dev)
         for l in range(wl.num_layers):
             g = wl.anchor_of[l]
             c.store_newest(l, new_kv[l], seq_lens, self.resident)
+            if self.paged and seq_lens_np is not None:
+                self.store_newest_resident(l, new_kv[l], seq_lens_np)
             if g == l:
                 for s in range(wl.spec):
-                    c.swap_in(l, topk[l][s], seq_lens, self.resident, None, self.out[l][s], plans[l][s])
+                    if self.paged:
+                        c.swap_in_paged(l, topk[l][s], seq_lens, self.block_table, wl.page_size,
+                                        self.hot_row_base, None, self.out[l][s], plans[l][s])
+                    else:
+                        c.swap_in(l, topk[l][s], seq_lens, self.resident, None, self.out[l][s], plans[l][s])
                     if after_swap_in is not None:
                         after_swap_in(l, s)
                 skips = [x for x in wl.skip_layers if wl.anchor_of[x] == l]

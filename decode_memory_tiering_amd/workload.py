@@ -41,6 +41,8 @@ class Workload:
     seq_first: Tuple = ("fixed", 8192)   # ("fixed", L) | ("uniform", lo, hi) | ("list", L_0, ..., L_R-1): L at step 0
     row_format: str = "bf16"         # "bf16" (576 x bf16) | "fp8_656"
     seed: int = 1
+    page_size: int = 0               # > 0: per-page residency with this page size
+    resident_page_frac: float = 0.0  # share of (request, page) pairs that are resident
 
     @property
     def anchors(self) -> Tuple[int, ...]:
@@ -70,6 +72,11 @@ WORKLOADS: Dict[str, Workload] = {
     "long_context": Workload("long_context", 1, (0,), R=32, B=4096, K=2048, rb=656,
                              steps=16, spec=3, topk_kind="uniform",
                              seq_first=("fixed", 131072), row_format="fp8_656", seed=5),
+    # per-page residency: a quarter of the 64-token pages of each request are
+    # resident, the rest host-backed holes (vLLM design note, "Resident device
+    # pages"); otherwise the DSV3.2-shaped decode of one layer
+    "paged_decode": Workload("paged_decode", 1, (0,), R=128, B=6144, K=2048, rb=1152, steps=32,
+                             seq_first=("fixed", 40000), seed=6, page_size=64, resident_page_frac=0.25),
 }
 
 
@@ -114,6 +121,22 @@ def resident_mask(wl: Workload) -> np.ndarray:
     if wl.n_resident:
         m[_rng(wl.seed, 7002).permutation(wl.R)[: wl.n_resident]] = 1
     return m
+
+
+def block_table(wl: Workload, steps: Optional[int] = None) -> Tuple[np.ndarray, int]:
+    """Per-page residency: [R][max_pages] physical page of each page, or -1
+    (host-backed).  A seeded share resident_page_frac of all (request, page)
+    pairs is resident, on distinct physical pages in a shuffled order.
+    Returns the table and the number of physical pages."""
+    assert wl.page_size > 0
+    ms = max_seq(wl, steps)
+    max_pages = (ms + wl.page_size - 1) // wl.page_size
+    rng = _rng(wl.seed, 7003)
+    n = wl.R * max_pages
+    n_res = int(round(wl.resident_page_frac * n))
+    flat = np.full(n, -1, np.int32)
+    flat[rng.choice(n, size=n_res, replace=False)] = rng.permutation(n_res).astype(np.int32)
+    return flat.reshape(wl.R, max_pages), n_res
 
 
 # ---------------------------------------------------------------------------

@@ -78,6 +78,7 @@ extern "C" {
 #define HISPARSE_DERR_REQ_IDX    0x8u  /* req_idx[b] outside [0, R) */
 #define HISPARSE_DERR_STATE      0x10u /* lru not a permutation / slot map not injective or out of range */
 #define HISPARSE_DERR_PLAN       0x20u /* replay: count > K, or a (pos, slot) pair out of range */
+#define HISPARSE_DERR_PAGE       0x40u /* paged: block-table entry < -1, or a physical row beyond INT32_MAX */
 
 /* hisparse_host_alloc flags */
 #define HISPARSE_HOST_DEFAULT     0u   /* HIP's default pinned, mapped allocation */
@@ -165,6 +166,32 @@ int hisparse_swap_in(hisparse_ctx* ctx, int32_t anchor_layer,
                      const int32_t* topk_idx, const int32_t* seq_lens,
                      const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb,
                      int32_t* out_slots, hisparse_plan plan_row, hipStream_t stream);
+
+/* The same fused resolver with per-page residency ([vLLM] "Resident device
+ * pages": resident pages are checked first, then hot rows, then pinned host
+ * memory; non-resident pages are host-backed holes).  block_table [nb]
+ * [max_pages] (device) holds, for page p of batch row b (positions
+ * [p*page_size, (p+1)*page_size)), the physical page in the caller's resident
+ * cache, or -1 for a host-backed page; pages at or beyond max_pages are
+ * host-backed (max_pages may be 0, block_table then NULL).  Output ids are
+ * rows of one view chosen by the caller, as in a packed resident + hot
+ * allocation ([vLLM] "Performance invariants"):
+ *   resident position t      block_table[b][t / page_size] * page_size + t % page_size
+ *   hot slot s (0..B, B = newest)   hot_row_base + r * (B + 1) + s
+ *   padding                  -1
+ * Resident positions never enter hit detection, the LRU, the plan or the
+ * copy; the newest token resolves in tier 0 when its page is resident.  With
+ * L <= B every non-resident position resolves to hot_row_base + r*(B+1) + t.
+ * There is no resident_mask: a fully resident request has every page in the
+ * table.  Host checks: page_size >= 1, max_pages >= 0, hot_row_base >= 0 and
+ * hot_row_base + R*(B+1) <= INT32_MAX (else HISPARSE_EINVAL).  A block-table
+ * entry below -1, or a physical row beyond INT32_MAX, fails the batch row
+ * (HISPARSE_DERR_PAGE), like every other device-side precondition. */
+int hisparse_swap_in_paged(hisparse_ctx* ctx, int32_t anchor_layer,
+                           const int32_t* topk_idx, const int32_t* seq_lens,
+                           const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                           int32_t hot_row_base, const int32_t* req_idx, int32_t nb,
+                           int32_t* out_rows, hisparse_plan plan_row, hipStream_t stream);
 
 /* Copy-only replay of an anchor's plan row on a skip layer: for each batch
  * row b and m < count[b], hot[skip][r][slot] <- host[skip][r][pos].  Runs on

@@ -37,6 +37,9 @@ class OracleRun:
         self.resident = W.resident_mask(wl)
         for g in wl.anchors:
             self.orc.admit(g, np.arange(wl.R), self.L0)
+        if wl.page_size > 0:
+            self.block_table, n_phys = W.block_table(wl, self.steps)
+            self.hot_row_base = n_phys * wl.page_size
 
     def _fill_cpu(self):
         import torch
@@ -58,7 +61,11 @@ class OracleRun:
             if g == l:
                 o, p = [], []
                 for s in range(wl.spec):
-                    out, plan = orc.swap_in(l, topk[l][s], L, res)
+                    if wl.page_size > 0:
+                        out, plan = orc.swap_in_paged(l, topk[l][s], L, self.block_table, wl.page_size,
+                                                      self.hot_row_base)
+                    else:
+                        out, plan = orc.swap_in(l, topk[l][s], L, res)
                     o.append(out)
                     p.append(plan)
                 outs[l] = np.stack(o)

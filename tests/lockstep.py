@@ -59,6 +59,10 @@ def run_lockstep(wl: W.Workload, steps: Optional[int] = None, *, block_size: int
         def after_swap_in(a, s):
             if not check_gather:
                 return
+            if g.paged:   # rows of the caller's view: resident cache, then hot buffer
+                view = g.row_view(a)
+                gathered[(a, s)] = view[g.out[a][s].clamp(0, view.shape[0] - 1).long().view(-1)].view(R, K, rb)
+                return
             # Resident rows resolve to positions in the caller's resident cache,
             # not to hot-buffer rows: they are not gathered (index 0 stands in).
             # Slot ids are compared exactly against the oracle elsewhere; the
@@ -69,7 +73,7 @@ def run_lockstep(wl: W.Workload, steps: Optional[int] = None, *, block_size: int
             rows = torch.arange(R, device=dev, dtype=torch.int64)[:, None] * (B + 1) + idx
             gathered[(a, s)] = g.cache.hot[a].view(R * (B + 1), rb)[rows.view(-1)].view(R, K, rb)
 
-        g.step(topk_dev, new_kv, g.seq_lens(k), after_swap_in=after_swap_in)
+        g.step(topk_dev, new_kv, g.seq_lens(k), after_swap_in=after_swap_in, seq_lens_np=L_np)
         outs, plans = o.step(k, topk, new_kv.cpu().numpy())
         torch.cuda.synchronize(dev)
         for a in wl.anchors:

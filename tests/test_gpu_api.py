@@ -256,3 +256,39 @@ def test_readmission_keeps_results_byte_correct():
         L = L + 1
     assert c.get_error() == 0
     c.close()
+
+
+def test_paged_bad_block_table_fails_the_row():
+    R, K, B = 3, 24, 64
+    c = _cache(R=R, K=K, B=B)
+    L = _slow_setup(c)
+    P, max_pages = 16, (c.max_seq + 15) // 16
+    bt = np.full((R, max_pages), -1, np.int32)
+    bt[:, 0] = [3, 4, 5]
+    bt[1, 2] = -5                                    # not a page, not a hole
+    rng = np.random.default_rng(8)
+    topk = np.stack([rng.choice(L, size=K, replace=False) for _ in range(R)]).astype(np.int32)
+    topk[1, 0] = 2 * P + 1                           # lands on the bad entry
+    out = torch.empty(R, K, dtype=torch.int32, device="cuda")
+    plan = H.Plan.empty(R, K)
+    lru0, tok0 = c.get_state(0)
+    c.swap_in_paged(0, _dev(topk), _dev(np.full(R, L, np.int32)), _dev(bt), P, 1000, None, out, plan)
+    torch.cuda.synchronize()
+    assert c.get_error() & H.HISPARSE_DERR_PAGE
+    o = out.cpu().numpy()
+    assert (o[1] == -1).all() and plan.count[1].item() == 0
+    assert (o[0] >= 0).all() and (o[2] >= 0).all()
+    lru, tok = c.get_state(0)
+    assert torch.equal(lru[1], lru0[1]) and torch.equal(tok[1], tok0[1])
+    c.close()
+
+
+def test_paged_host_checks():
+    c = _cache()
+    t = torch.zeros(1, c.K, dtype=torch.int32, device="cuda")
+    L = torch.full((1,), 10, dtype=torch.int32, device="cuda")
+    for kw in (dict(page_size=0, hot_row_base=0), dict(page_size=4, hot_row_base=-1),
+               dict(page_size=4, hot_row_base=2 ** 31 - 10)):
+        with pytest.raises(H.HisparseError):
+            c.swap_in_paged(0, t, L, None, kw["page_size"], kw["hot_row_base"], None, t.clone(), H.Plan.empty(1, c.K))
+    c.close()

@@ -126,3 +126,27 @@ def test_replay_grid_sizes():
                     seq_first=("uniform", 200, 5000), seed=24)
     for g in (1, 5, 64):
         _lockstep(wl, replay_grid=g, prefetch=True)
+
+
+# -- per-page residency ----------------------------------------------------------
+PAGED = [
+    W.Workload("paged_a", 2, (0, 0), R=6, B=300, K=100, rb=48, steps=10, page_size=16,
+               resident_page_frac=0.3, seq_first=("uniform", 100, 3000), seed=31),
+    W.Workload("paged_none", 1, (0,), R=5, B=256, K=64, rb=32, steps=8, page_size=8,
+               resident_page_frac=0.0, seq_first=("uniform", 100, 2000), seed=32),
+    W.Workload("paged_all", 1, (0,), R=4, B=256, K=64, rb=32, steps=6, page_size=32,
+               resident_page_frac=1.0, seq_first=("uniform", 100, 2000), seed=33),
+    W.Workload("paged_spec", 1, (0,), R=5, B=512, K=200, rb=656, steps=6, spec=3, page_size=7,
+               resident_page_frac=0.5, seq_first=("uniform", 300, 5000), topk_kind="uniform",
+               row_format="fp8_656", seed=34),
+]
+
+
+@pytest.mark.parametrize("wl", PAGED, ids=[w.name for w in PAGED])
+def test_paged_geometries(wl):
+    _lockstep(wl)
+
+
+@pytest.mark.timeout(600)
+def test_paged_decode_full():
+    _lockstep(W.WORKLOADS["paged_decode"], progress=True, compare_state_every=4)
