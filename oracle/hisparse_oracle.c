@@ -440,3 +440,38 @@ int orc_backup(int32_t R, int32_t B, int64_t rb, int32_t max_seq,
     }
     return ORC_OK;
 }
+
+/* Page transfers (vLLM design note, "Spill transaction": a resident page's
+ * contents are copied to its host page before the resident block is reused;
+ * "P/D import target": an import copies a bounded device staging pool into
+ * registered host memory and mirrors the pages needed right away into
+ * resident destinations during that copy).  A transfer carries physical copy
+ * coordinates only: (source page, request, host page, mirror page or -1).
+ * A page holds page_size consecutive positions; a host page that runs past
+ * max_seq is copied up to max_seq.  src holds src_pages pages, mirror holds
+ * mirror_pages pages, host is [R][max_seq][rb]. */
+int orc_page_copy(int32_t R, int32_t max_seq, int64_t rb, int32_t page_size,
+                  const uint8_t* src, int32_t src_pages,
+                  uint8_t* host, uint8_t* mirror, int32_t mirror_pages,
+                  int32_t n, const int32_t* transfers)
+{
+    if (R <= 0 || max_seq <= 0 || rb <= 0 || page_size <= 0 || n < 0 || !src || !host)
+        return ORC_EINVAL;
+    for (int32_t x = 0; x < n; ++x) {
+        int32_t sp = transfers[4 * x + 0];
+        int32_t r = transfers[4 * x + 1];
+        int32_t hp = transfers[4 * x + 2];
+        int32_t mp = transfers[4 * x + 3];
+        if (sp < 0 || sp >= src_pages || r < 0 || r >= R || hp < 0 ||
+            (int64_t)hp * page_size >= max_seq || mp < -1 || mp >= mirror_pages || (mp >= 0 && !mirror))
+            return ORC_EPRECOND;
+        int64_t rows = max_seq - (int64_t)hp * page_size;
+        if (rows > page_size)
+            rows = page_size;
+        const uint8_t* from = src + (int64_t)sp * page_size * rb;
+        memcpy(host + ((int64_t)r * max_seq + (int64_t)hp * page_size) * rb, from, (size_t)(rows * rb));
+        if (mp >= 0)
+            memcpy(mirror + (int64_t)mp * page_size * rb, from, (size_t)(rows * rb));
+    }
+    return ORC_OK;
+}

@@ -103,6 +103,14 @@ int orc_backup(int32_t R, int32_t B, int64_t rb, int32_t max_seq,
                const int32_t* seq_lens, const uint8_t* resident_mask,
                const uint8_t* hot, uint8_t* host);
 
+/* Page transfers: spill (resident page -> host page) and host import
+ * (staging page -> host page, optionally mirrored into a resident page).
+ * transfers [n][4] = (source page, request, host page, mirror page or -1). */
+int orc_page_copy(int32_t R, int32_t max_seq, int64_t rb, int32_t page_size,
+                  const uint8_t* src, int32_t src_pages,
+                  uint8_t* host, uint8_t* mirror, int32_t mirror_pages,
+                  int32_t n, const int32_t* transfers);
+
 #ifdef __cplusplus
 }
 #endif

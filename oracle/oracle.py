@@ -68,11 +68,12 @@ def load_oracle(path: str = LIB) -> ctypes.CDLL:
                                 _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.orc_swap_in_paged.argtypes = [_I32, _I32, _I32, _I64, _I32, _I32, _P,
                                       _P, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.orc_page_copy.argtypes = [_I32, _I32, _I64, _I32, _P, _I32, _P, _P, _I32, _I32, _P]
     lib.orc_replay.argtypes = [_I32, _I32, _I32, _I64, _I32, _I32, _P,
                                _P, _P, _P, _P, _P]
     lib.orc_backup.argtypes = [_I32, _I32, _I64, _I32, _I32, _P, _P, _P, _P, _P]
     for fn in ("orc_admit_state", "orc_admit_fill", "orc_store_newest",
-               "orc_swap_in_row", "orc_swap_in", "orc_swap_in_paged", "orc_replay", "orc_backup"):
+               "orc_swap_in_row", "orc_swap_in", "orc_swap_in_paged", "orc_page_copy", "orc_replay", "orc_backup"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -210,6 +211,19 @@ class Oracle:
             _ptr(plan.pos), _ptr(plan.slot), _ptr(plan.count))
         self._check(rc, "swap_in_paged")
         return out, plan
+
+    def page_copy(self, layer: int, page_size: int, src: np.ndarray, transfers, mirror: Optional[np.ndarray] = None):
+        """Spill / host import: src [src_pages*P][rb] (resident cache or
+        staging pool) -> host pool pages, optionally mirrored into mirror
+        [mirror_pages*P][rb].  transfers [n][4] = (src page, request, host
+        page, mirror page or -1)."""
+        tr = _i32(transfers).reshape(-1, 4)
+        src = _u8(src)
+        rc = self.lib.orc_page_copy(
+            self.R, self.max_seq, self.rb, int(page_size), _ptr(src), src.shape[0] // page_size,
+            _ptr(self.host[layer]), _ptr(mirror), 0 if mirror is None else mirror.shape[0] // page_size,
+            tr.shape[0], _ptr(tr))
+        self._check(rc, "page_copy")
 
     def replay(self, skip_layer: int, plan: Plan, req_idx=None):
         ridx = _i32(req_idx) if req_idx is not None else None

@@ -26,6 +26,11 @@ What each pin rests on:
     and moves nothing; no page resident gives the per-request resolver's
     result; and in the caller's combined row view every resolved row holds
     the position's KV while resident positions never reach the hot tiers.
+  * pin_spill_round_trip / pin_import_mirror: page transfers (vLLM design
+    note, "Spill transaction" and "P/D import target"): the copied pages
+    equal their sources, nothing else changes, a page past the pool is cut,
+    and after the table entry is replaced the resolver still returns every
+    position's KV.
 """
 from __future__ import annotations
 
@@ -513,6 +518,110 @@ def pin_paged_bytes(lib, steps: int = 10) -> List[str]:
     return fails
 
 
+# ---------------------------------------------------------------------------
+# page transfers: spill and host import
+# ---------------------------------------------------------------------------
+def _paged_steps(orc, bt, res_cache, rng, L0, k0, steps, P, fails, label):
+    """Paged resolve steps with the combined-view byte check."""
+    R, K, B = orc.R, orc.K, orc.B
+    base = res_cache.shape[0]
+    for k in range(k0, k0 + steps):
+        L = L0 + 1 + k
+        topk = np.stack([rng.choice(int(L[r]), min(K, int(L[r])), replace=False) for r in range(R)]).astype(np.int32)
+        nk = _new_kv(R, L)
+        orc.store_newest(0, nk, L)
+        for r in range(R):
+            pg = (int(L[r]) - 1) // P
+            if bt[r, pg] >= 0:
+                res_cache[bt[r, pg] * P + (int(L[r]) - 1) % P] = nk[r]
+        out, _ = orc.swap_in_paged(0, topk, L, bt, P, base)
+        view = np.concatenate([res_cache, orc.hot[0].reshape(R * (B + 1), RB)])
+        for r in range(R):
+            for i in range(K):
+                t = int(topk[r, i])
+                want = nk[r] if t == L[r] - 1 else orc.host[0][r, t]
+                if not np.array_equal(view[out[r, i]], want):
+                    fails.append(f"{label}: step {k} r {r}: row {out[r, i]} does not hold position {t}")
+                    return
+        orc.backup(0, L)
+
+
+def pin_spill_round_trip(lib) -> List[str]:
+    """Spill resident pages to their host pages (whose old contents are
+    poisoned first), mark them host-backed, keep resolving: every position
+    still resolves to its KV, now through the hot tiers."""
+    fails = []
+    R, B, K, P, steps = 4, 24, 10, 4, 4
+    L0 = np.array([30, 45, 70, 100], np.int32)
+    orc, bt, res_cache, rng, max_seq = _paged_setup(lib, R, B, K, P, L0, 2 * steps + 1, 0.5, 21)
+    _paged_steps(orc, bt, res_cache, rng, L0, 0, steps, P, fails, "spill (before)")
+    rr, pp = np.nonzero(bt >= 0)
+    pick = rng.choice(rr.size, size=rr.size // 2, replace=False)
+    transfers = []
+    for q in pick:
+        r, pg = int(rr[q]), int(pp[q])
+        lo, hi = pg * P, min(pg * P + P, max_seq)
+        orc.host[0][r, lo:hi] = 0x5A                      # stale host page
+        transfers.append((int(bt[r, pg]), r, pg, -1))
+    before = orc.host[0].copy()
+    orc.page_copy(0, P, res_cache, transfers)
+    for sp, r, pg, _ in transfers:
+        lo, hi = pg * P, min(pg * P + P, max_seq)
+        if not np.array_equal(orc.host[0][r, lo:hi], res_cache[sp * P: sp * P + hi - lo]):
+            fails.append(f"spill: host page {pg} of request {r} != resident page {sp}")
+        before[r, lo:hi] = orc.host[0][r, lo:hi]
+    if not np.array_equal(before, orc.host[0]):
+        fails.append("spill: rows outside the spilled pages changed")
+    for sp, r, pg, _ in transfers:
+        bt[r, pg] = -1                                    # the table entry is replaced
+    _paged_steps(orc, bt, res_cache, rng, L0, steps, steps, P, fails, "spill (after)")
+    return fails
+
+
+def pin_import_mirror(lib) -> List[str]:
+    """Import staging pages into host pages (the last one past max_seq is cut),
+    mirroring some into resident pages; mark the mirrored pages resident and
+    keep resolving."""
+    fails = []
+    R, B, K, P, steps = 3, 16, 8, 8, 3
+    L0 = np.array([20, 40, 60], np.int32)
+    orc, bt, res_cache, rng, max_seq = _paged_setup(lib, R, B, K, P, L0, steps + 1, 0.0, 22, n_phys_extra=12)
+    max_pages = bt.shape[1]
+    staging = rng.integers(0, 256, size=(10 * P, RB), dtype=np.uint8)
+    transfers, mirrored = [], []
+    for x, (r, pg) in enumerate([(0, 0), (0, 2), (1, 1), (1, 3), (2, 0), (2, max_pages - 1), (0, 1)]):
+        mp = x if x % 2 == 0 else -1
+        transfers.append((x, r, pg, mp))
+        if mp >= 0:
+            mirrored.append((r, pg, mp))
+    before = orc.host[0].copy()
+    orc.page_copy(0, P, staging, transfers, mirror=res_cache)
+    for sp, r, pg, mp in transfers:
+        lo, hi = pg * P, min(pg * P + P, max_seq)
+        want = staging[sp * P: sp * P + hi - lo]
+        if not np.array_equal(orc.host[0][r, lo:hi], want):
+            fails.append(f"import: host page {pg} of request {r} != staging page {sp}")
+        if mp >= 0 and not np.array_equal(res_cache[mp * P: mp * P + hi - lo], want):
+            fails.append(f"import: mirror page {mp} != staging page {sp}")
+        before[r, lo:hi] = orc.host[0][r, lo:hi]
+    if not np.array_equal(before, orc.host[0]):
+        fails.append("import: rows outside the imported pages changed")
+    for r, pg, mp in mirrored:
+        bt[r, pg] = mp
+    _paged_steps(orc, bt, res_cache, rng, L0, 0, steps, P, fails, "import")
+    try:
+        orc.page_copy(0, P, staging, [(0, R, 0, -1)])
+        fails.append("import: request out of range accepted")
+    except OracleError:
+        pass
+    try:
+        orc.page_copy(0, P, staging, [(0, 0, max_pages, -1)])
+        fails.append("import: host page past the pool accepted")
+    except OracleError:
+        pass
+    return fails
+
+
 # cheapest first: a planted mistake is usually caught within milliseconds
 ALL_PINS = {
     "hand_trace": pin_hand_trace,
@@ -523,6 +632,8 @@ ALL_PINS = {
     "paged_hand_trace": pin_paged_hand_trace,
     "paged_closed_forms": pin_paged_closed_forms,
     "paged_bytes": pin_paged_bytes,
+    "spill_round_trip": pin_spill_round_trip,
+    "import_mirror": pin_import_mirror,
     "textbook_lru_random": pin_textbook_lru_random,
     "textbook_lru_exhaustive": pin_textbook_lru_exhaustive,
 }

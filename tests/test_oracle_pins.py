@@ -9,11 +9,13 @@ unnoticed.  The mutants are compiled from text edits of
 never modified.
 """
 import os
+import subprocess
+import sys
 import tempfile
 
 import pytest
 
-from oracle.oracle import SRC, build_oracle, load_oracle
+from oracle.oracle import SRC, build_oracle
 import oracle_pins
 
 
@@ -73,6 +75,13 @@ MUTANTS = [
      "int32_t phys = pg < max_pages ? block_row[pg] : 0;"),
     ("physical page 0 not resident", "if (phys >= 0) {\n            res_row", "if (phys > 0) {\n            res_row"),
     ("hot base of request 0 used for all", "hot_row_base + (int64_t)r * (B + 1),", "hot_row_base,"),
+    ("page transfer not cut at the pool end", "        if (rows > page_size)\n            rows = page_size;",
+     "        rows = page_size;"),
+    ("mirror skipped", "        if (mp >= 0)\n            memcpy(mirror", "        if (mp > 0)\n            memcpy(mirror"),
+    ("host page ignores the request", "memcpy(host + ((int64_t)r * max_seq + (int64_t)hp * page_size) * rb, from,",
+     "memcpy(host + ((int64_t)hp * page_size) * rb, from,"),
+    ("source page offset dropped", "const uint8_t* from = src + (int64_t)sp * page_size * rb;",
+     "const uint8_t* from = src;"),
 ]
 
 
@@ -82,22 +91,37 @@ def oracle_source():
         return f.read()
 
 
+_RUN_PINS = r"""
+import sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+from oracle.oracle import load_oracle
+import oracle_pins
+lib = load_oracle({lib!r})
+for name, pin in oracle_pins.ALL_PINS.items():
+    try:
+        fails = pin(lib)
+    except Exception as e:
+        fails = [repr(e)]
+    if fails:
+        print("caught by", name, ":", fails[0][:200])
+        sys.exit(3)
+sys.exit(0)
+"""
+
+
 @pytest.mark.parametrize("label,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_planted_mistake_is_caught(oracle_source, label, old, new):
+    """Each mutant runs the pins in a child process: a pin failing, an oracle
+    error or a crash of the mutant (a planted overrun can abort) all count as
+    caught; only a clean pass of every pin does not."""
     assert oracle_source.count(old) == 1, f"mutation site for '{label}' not found exactly once"
+    tests_dir = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(tests_dir)
     with tempfile.TemporaryDirectory() as d:
         src = os.path.join(d, "mutant.c")
         with open(src, "w") as f:
             f.write(oracle_source.replace(old, new))
-        lib = load_oracle(build_oracle(src=src, out=os.path.join(d, "libmutant.so"),
-                                       extra_flags=["-I", os.path.dirname(SRC)]))
-        caught = []
-        for name, pin in oracle_pins.ALL_PINS.items():
-            try:
-                fails = pin(lib)
-            except Exception as e:  # an oracle error under a mutant also counts as caught
-                fails = [f"{type(e).__name__}: {e}"]
-            if fails:
-                caught.append(name)
-                break
-        assert caught, f"planted mistake '{label}' passed every pin"
+        lib = build_oracle(src=src, out=os.path.join(d, "libmutant.so"), extra_flags=["-I", os.path.dirname(SRC)])
+        code = _RUN_PINS.format(root=root, tests=tests_dir, lib=lib)
+        res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+        assert res.returncode != 0, f"planted mistake '{label}' passed every pin"
