@@ -104,6 +104,52 @@ def cpu_baseline(wl, steps, host_pools, topk_all, newkv_all, budget_s=20.0):
                        f"and {wl.num_layers} layer(s), single thread, oracle time {t_run:.2f}s")
 
 
+def measure_page_copy(dev, W, args):
+    """Spill (resident page -> host page) and host import (staging page ->
+    host page, half mirrored to resident pages) on the paged decode's shape:
+    64-token pages of 1152-byte rows, 4096 pages per call."""
+    import torch
+    from decode_memory_tiering_amd.runner import GpuRun
+    wl = W.WORKLOADS["paged_decode"]
+    g = GpuRun(wl, 2, fill=False)
+    P, rb, n = wl.page_size, wl.rb, 4096
+    rng = np.random.default_rng(0)
+    max_pages = g.block_table_np.shape[1]
+    n_res = g.res_cache[0].shape[0] // P
+    pick = rng.choice(wl.R * max_pages, size=n, replace=False)
+    spill = np.stack([rng.choice(n_res, n, replace=False), pick // max_pages, pick % max_pages,
+                      -np.ones(n, np.int64)], 1).astype(np.int32)
+    stg = torch.randint(0, 255, (n * P, rb), dtype=torch.uint8, device=dev)
+    mirror = np.where(np.arange(n) % 2 == 0, rng.choice(n_res, n, replace=False), -1)
+    imp = np.stack([np.arange(n), pick // max_pages, pick % max_pages, mirror], 1).astype(np.int32)
+    spill_d, imp_d = torch.from_numpy(spill).to(dev), torch.from_numpy(imp).to(dev)
+    out = {}
+    for name, fn, nbytes in (("spill", lambda: g.cache.spill(0, g.res_cache[0], P, spill_d), n * P * rb),
+                             ("import", lambda: g.cache.import_pages(0, stg, P, g.res_cache[0], imp_d), n * P * rb)):
+        fn()
+        torch.cuda.synchronize(dev)
+        times = []
+        for _ in range(max(args.steps, 3)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize(dev)
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        t = float(np.mean(times))
+        out[name] = dict(pages=n, bytes_to_host=nbytes, mean_us=t * 1e6, gbps=nbytes / t / 1e9)
+    err = g.cache.get_error()
+    g.close()
+    if err:
+        log(f"[bench] device error word {err:#x}")
+        sys.exit(1)
+    print(json.dumps({"metric": "page transfer GB/s (device -> pinned host)", "value": out["spill"]["gbps"],
+                      "unit": "GB/s", "higher_is_better": True, "n_gpus": 1, "steps": max(args.steps, 3),
+                      "config": {"workload": "paged_decode pages", "page_size": P, "row_bytes": rb},
+                      "spill": out["spill"], "import": out["import"],
+                      "peak": PCIE5_X16_GBPS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +164,8 @@ def main():
     ap.add_argument("--layer-compute-mib", type=int, default=0,
                     help="stand-in for each layer's other compute: a device copy of this many MiB on the "
                          "main stream after every layer (the IndexShare overlap case uses 2048)")
+    ap.add_argument("--measure", default="step", choices=["step", "page_copy"],
+                    help="page_copy: time spill and host import of paged_decode-shaped pages instead of decode steps")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -143,6 +191,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize(dev)
         print(json.dumps({"calibration_copy_bytes": n, "launches": 5}), flush=True)
+        return
+    if args.measure == "page_copy":
+        measure_page_copy(dev, W, args)
         return
     wl = W.WORKLOADS[args.workload]
     total = args.warmup + args.steps

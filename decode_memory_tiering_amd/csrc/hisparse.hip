@@ -717,6 +717,57 @@ __global__ __launch_bounds__(64) void backup_kernel(RowArgs a)
                  a.host + (size_t(r) * a.max_seq + (L - 1)) * a.rb, a.rb);
 }
 
+// Page transfers: spill (resident page -> host page) and host import
+// (staging page -> host page, mirrored into a resident page when asked).
+// transfers [n][4] = (source page, request, host page, mirror page or -1);
+// a page is page_size consecutive positions, cut at max_seq.  Each
+// workgroup copies whole pages (contiguous rows on both sides); a transfer
+// with a coordinate out of range is skipped and sets HISPARSE_DERR_PAGE.
+struct PageCopyArgs {
+    const uint8_t* src;          // [src_pages * P][rb], device
+    uint8_t* host;               // [R][max_seq][rb], pinned host
+    uint8_t* mirror;             // [mirror_pages * P][rb], device, or null
+    const int32_t* transfers;
+    uint32_t* err;
+    int32_t src_pages, mirror_pages, n, R, max_seq, rb, P;
+};
+
+__global__ __launch_bounds__(256) void page_copy_kernel(PageCopyArgs a)
+{
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    for (int x = blockIdx.x; x < a.n; x += gridDim.x) {
+        const int sp = a.transfers[4 * x + 0], r = a.transfers[4 * x + 1];
+        const int hp = a.transfers[4 * x + 2], mp = a.transfers[4 * x + 3];
+        const bool ok = sp >= 0 && sp < a.src_pages && r >= 0 && r < a.R && hp >= 0 &&
+                        static_cast<long long>(hp) * a.P < a.max_seq && mp >= -1 && mp < a.mirror_pages;
+        if (!ok) {
+            if (tid == 0) atomicOr(a.err, HISPARSE_DERR_PAGE);
+            continue;
+        }
+        const int rows = a.max_seq - hp * a.P < a.P ? a.max_seq - hp * a.P : a.P;
+        const int chunks = rows * (a.rb >> 4);
+        const uint8_t* src = a.src + size_t(sp) * a.P * a.rb;
+        uint8_t* dst = a.host + (size_t(r) * a.max_seq + size_t(hp) * a.P) * a.rb;
+        uint8_t* mdst = mp >= 0 ? a.mirror + size_t(mp) * a.P * a.rb : nullptr;
+        for (int c0 = tid; c0 < chunks; c0 += kCopyUnroll * nthr) {
+            u32x4 v[kCopyUnroll];
+#pragma unroll
+            for (int u = 0; u < kCopyUnroll; ++u) {
+                const int c = c0 + u * nthr;
+                if (c < chunks) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t(c) << 4)));
+            }
+#pragma unroll
+            for (int u = 0; u < kCopyUnroll; ++u) {
+                const int c = c0 + u * nthr;
+                if (c < chunks) {
+                    *reinterpret_cast<u32x4*>(dst + (size_t(c) << 4)) = v[u];
+                    if (mdst) *reinterpret_cast<u32x4*>(mdst + (size_t(c) << 4)) = v[u];
+                }
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void init_state_kernel(int32_t* lru, int32_t* tok, int R, int B)
 {
     const size_t n = size_t(R) * B;
@@ -1080,6 +1131,43 @@ int hisparse_replay_plan(hisparse_ctx* c, int32_t skip_layer, hisparse_plan plan
     a.nb = nb; a.R = c->R; a.B = c->B; a.K = c->K; a.rb = c->rb; a.max_seq = c->max_seq;
     hipLaunchKernelGGL(replay_kernel, dim3(c->replay_grid), dim3(256), replay_lds_bytes(nb), side_stream, a);
     return hip_rc(hipGetLastError());
+}
+
+namespace {
+
+constexpr int kPageCopyGrid = 256;
+
+int launch_page_copy(hisparse_ctx* c, int32_t layer, const void* src, int32_t src_pages, int32_t page_size,
+                     void* mirror, int32_t mirror_pages, const int32_t* transfers, int32_t n, hipStream_t stream)
+{
+    if (!c || layer < 0 || layer >= c->layers || n < 0 || page_size < 1 || src_pages < 0 || mirror_pages < 0)
+        return HISPARSE_EINVAL;
+    if (n == 0) return HISPARSE_OK;
+    if (!src || !transfers || !aligned16(src) || (mirror_pages > 0 && (!mirror || !aligned16(mirror))))
+        return HISPARSE_EINVAL;
+    PageCopyArgs a{};
+    a.src = static_cast<const uint8_t*>(src); a.host = const_cast<uint8_t*>(c->host[layer]);
+    a.mirror = mirror_pages > 0 ? static_cast<uint8_t*>(mirror) : nullptr; a.transfers = transfers; a.err = c->err;
+    a.src_pages = src_pages; a.mirror_pages = mirror_pages; a.n = n; a.R = c->R; a.max_seq = c->max_seq;
+    a.rb = c->rb; a.P = page_size;
+    hipLaunchKernelGGL(page_copy_kernel, dim3(n < kPageCopyGrid ? n : kPageCopyGrid), dim3(256), 0, stream, a);
+    return hip_rc(hipGetLastError());
+}
+
+}  // namespace
+
+int hisparse_spill(hisparse_ctx* c, int32_t layer, const void* resident_cache, int32_t resident_pages,
+                   int32_t page_size, const int32_t* transfers, int32_t n, hipStream_t stream)
+{
+    return launch_page_copy(c, layer, resident_cache, resident_pages, page_size, nullptr, 0, transfers, n, stream);
+}
+
+int hisparse_import(hisparse_ctx* c, int32_t layer, const void* staging, int32_t staging_pages, int32_t page_size,
+                    void* resident_cache, int32_t resident_pages, const int32_t* transfers, int32_t n,
+                    hipStream_t stream)
+{
+    return launch_page_copy(c, layer, staging, staging_pages, page_size, resident_cache, resident_pages, transfers,
+                            n, stream);
 }
 
 int hisparse_backup(hisparse_ctx* c, int32_t layer, const int32_t* seq_lens, const uint8_t* resident_mask,

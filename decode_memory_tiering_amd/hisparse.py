@@ -36,7 +36,7 @@ HISPARSE_HOST_NONCOHERENT = 2
 # every entry point include/hisparse.h declares
 EXPORTS = (
     "hisparse_init", "hisparse_destroy", "hisparse_admit", "hisparse_store_newest",
-    "hisparse_swap_in", "hisparse_swap_in_paged", "hisparse_replay_plan", "hisparse_backup", "hisparse_get_state",
+    "hisparse_swap_in", "hisparse_swap_in_paged", "hisparse_replay_plan", "hisparse_backup", "hisparse_spill", "hisparse_import", "hisparse_get_state",
     "hisparse_set_state", "hisparse_get_error", "hisparse_host_alloc", "hisparse_host_free",
     "hisparse_swap_in_lds_bytes", "hisparse_strerror", "hisparse_version",
 )
@@ -94,6 +94,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hisparse_swap_in_paged.argtypes = [P, I32, P, P, P, I32, I32, I32, P, I32, P, hisparse_plan, P]
     lib.hisparse_replay_plan.argtypes = [P, I32, hisparse_plan, P, I32, P]
     lib.hisparse_backup.argtypes = [P, I32, P, P, P, I32, P]
+    lib.hisparse_spill.argtypes = [P, I32, P, I32, I32, P, I32, P]
+    lib.hisparse_import.argtypes = [P, I32, P, I32, I32, P, I32, P, I32, P]
     lib.hisparse_get_state.argtypes = [P, I32, P, P, P]
     lib.hisparse_set_state.argtypes = [P, I32, P, P, P]
     lib.hisparse_get_error.argtypes = [P, ctypes.POINTER(U32), ctypes.c_int, P]
@@ -223,6 +225,19 @@ def hisparse_backup(ctx: int, layer: int, seq_lens, resident_mask=None, req_idx=
                                   int(seq_lens.shape[0]), _stream(stream)), "hisparse_backup")
 
 
+def hisparse_spill(ctx: int, layer: int, resident_cache, page_size: int, transfers, stream=None) -> None:
+    pages = int(resident_cache.shape[0]) // page_size
+    _check(_lib().hisparse_spill(ctx, layer, _ptr(resident_cache), pages, page_size, _ptr(transfers),
+                                 int(transfers.shape[0]), _stream(stream)), "hisparse_spill")
+
+
+def hisparse_import(ctx: int, layer: int, staging, page_size: int, resident_cache, transfers, stream=None) -> None:
+    rpages = 0 if resident_cache is None else int(resident_cache.shape[0]) // page_size
+    _check(_lib().hisparse_import(ctx, layer, _ptr(staging), int(staging.shape[0]) // page_size, page_size,
+                                  _ptr(resident_cache), rpages, _ptr(transfers), int(transfers.shape[0]),
+                                  _stream(stream)), "hisparse_import")
+
+
 def hisparse_get_state(ctx: int, anchor_layer: int, lru, slot_tok, stream=None) -> None:
     _check(_lib().hisparse_get_state(ctx, anchor_layer, _ptr(lru), _ptr(slot_tok), _stream(stream)),
            "hisparse_get_state")
@@ -322,6 +337,12 @@ class HiSparseCache:
 
     def backup(self, layer, seq_lens, resident_mask=None, req_idx=None, stream=None):
         hisparse_backup(self.ctx, layer, seq_lens, resident_mask, req_idx, stream)
+
+    def spill(self, layer, resident_cache, page_size, transfers, stream=None):
+        hisparse_spill(self.ctx, layer, resident_cache, page_size, transfers, stream)
+
+    def import_pages(self, layer, staging, page_size, resident_cache, transfers, stream=None):
+        hisparse_import(self.ctx, layer, staging, page_size, resident_cache, transfers, stream)
 
     def get_state(self, anchor, stream=None):
         import torch

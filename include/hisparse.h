@@ -78,7 +78,8 @@ extern "C" {
 #define HISPARSE_DERR_REQ_IDX    0x8u  /* req_idx[b] outside [0, R) */
 #define HISPARSE_DERR_STATE      0x10u /* lru not a permutation / slot map not injective or out of range */
 #define HISPARSE_DERR_PLAN       0x20u /* replay: count > K, or a (pos, slot) pair out of range */
-#define HISPARSE_DERR_PAGE       0x40u /* paged: block-table entry < -1, or a physical row beyond INT32_MAX */
+#define HISPARSE_DERR_PAGE       0x40u /* paged: block-table entry < -1, or a physical row beyond INT32_MAX;
+                                          spill / import: a transfer coordinate out of range */
 
 /* hisparse_host_alloc flags */
 #define HISPARSE_HOST_DEFAULT     0u   /* HIP's default pinned, mapped allocation */
@@ -213,6 +214,31 @@ int hisparse_replay_plan(hisparse_ctx* ctx, int32_t skip_layer, hisparse_plan pl
 int hisparse_backup(hisparse_ctx* ctx, int32_t layer, const int32_t* seq_lens,
                     const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb,
                     hipStream_t stream);
+
+/* Spill ([vLLM] "Spill transaction"): before a resident block is reused,
+ * its contents are copied to the request's host page.  resident_cache
+ * (device) holds resident_pages pages of page_size rows of rb bytes;
+ * transfers [n][4] (device) = (resident page, request, host page, -1), the
+ * physical copy coordinates only.  Host page hp of request r is rows
+ * [hp*page_size, (hp+1)*page_size) of its host pool, cut at max_seq_len.
+ * "Enqueued" is this call's return (stream order protects the resident page
+ * from later work on the stream); "completed" is an event the caller
+ * records after it on the same stream, after which the host page may be
+ * published and the table entry replaced by -1.  A transfer with a
+ * coordinate out of range is skipped and sets HISPARSE_DERR_PAGE. */
+int hisparse_spill(hisparse_ctx* ctx, int32_t layer, const void* resident_cache, int32_t resident_pages,
+                   int32_t page_size, const int32_t* transfers, int32_t n, hipStream_t stream);
+
+/* Host import ([vLLM] "P/D import target"): pages arrive in a bounded
+ * device staging pool (staging_pages pages) and are copied into registered
+ * host memory; a page needed right away is mirrored into a resident page in
+ * the same pass.  transfers [n][4] (device) = (staging page, request, host
+ * page, resident page or -1).  resident_cache may be NULL when
+ * resident_pages is 0.  Out-of-range transfers are skipped
+ * (HISPARSE_DERR_PAGE). */
+int hisparse_import(hisparse_ctx* ctx, int32_t layer, const void* staging, int32_t staging_pages,
+                    int32_t page_size, void* resident_cache, int32_t resident_pages,
+                    const int32_t* transfers, int32_t n, hipStream_t stream);
 
 /* Copy an anchor layer's state out of / into the library ([R][B] int32 each,
  * device pointers).  For tests and checkpointing; asynchronous on stream. */

@@ -292,3 +292,104 @@ def test_paged_host_checks():
         with pytest.raises(H.HisparseError):
             c.swap_in_paged(0, t, L, None, kw["page_size"], kw["hot_row_base"], None, t.clone(), H.Plan.empty(1, c.K))
     c.close()
+
+
+# -- page transfers: spill and host import -----------------------------------------
+def test_page_copy_parity():
+    """Spill and import against the oracle; a page past the pool end is cut, bad
+    transfers are skipped with HISPARSE_DERR_PAGE."""
+    R, B, K, rb, P = 4, 64, 24, 48, 16
+    max_seq = 200                                  # last page (12) holds 8 rows
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
+    o = _oracle_for(c)
+    rng = np.random.default_rng(5)
+    res = rng.integers(0, 256, size=(20 * P, rb), dtype=np.uint8)
+    stg = rng.integers(0, 256, size=(10 * P, rb), dtype=np.uint8)
+    mirror_np = np.zeros((20 * P, rb), np.uint8)
+    spill = np.array([(3, 0, 0, -1), (7, 1, 12, -1), (0, 3, 5, -1), (19, 2, 1, -1)], np.int32)
+    imp = np.array([(0, 0, 3, 4), (9, 2, 12, -1), (5, 1, 7, 19), (1, 3, 0, -1)], np.int32)
+    bad = np.array([(20, 0, 0, -1), (0, R, 0, -1), (0, 0, 13, -1), (0, 0, 0, 20)], np.int32)
+    res_d, stg_d = _dev(res, torch.uint8), _dev(stg, torch.uint8)
+    mirror_d = torch.zeros(20 * P, rb, dtype=torch.uint8, device="cuda")
+    c.spill(0, res_d, P, _dev(spill))
+    c.import_pages(0, stg_d, P, mirror_d, _dev(imp))
+    torch.cuda.synchronize()
+    assert c.get_error() == 0
+    o.page_copy(0, P, res, spill)
+    o.page_copy(0, P, stg, imp, mirror=mirror_np)
+    assert np.array_equal(c.host_np[0], o.host[0])
+    assert np.array_equal(mirror_d.cpu().numpy(), mirror_np)
+    host0 = c.host_np[0].copy()
+    c.import_pages(0, stg_d, P, mirror_d, _dev(bad))
+    torch.cuda.synchronize()
+    assert c.get_error() & H.HISPARSE_DERR_PAGE
+    assert np.array_equal(c.host_np[0], host0)
+    c.close()
+
+
+def test_spill_mid_decode_round_trip():
+    """A paged decode on GPU and oracle side by side; halfway, half of the
+    resident pages are spilled and become host-backed; every output, state,
+    hot buffer and host pool stays identical, and every resolved row of the
+    combined view holds the position's KV."""
+    R, B, K, rb, P, steps = 4, 64, 24, 32, 8, 10
+    L0 = np.array([40, 70, 120, 300], np.int32)
+    max_seq = int(L0.max()) + steps + 1
+    max_pages = (max_seq + P - 1) // P
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
+    o = _oracle_for(c)
+    rng = np.random.default_rng(6)
+    bt = np.full((R, max_pages), -1, np.int32)
+    flat = rng.choice(R * max_pages, size=R * max_pages // 2, replace=False)
+    bt.reshape(-1)[flat] = rng.permutation(flat.size)
+    n_phys = flat.size
+    res = np.zeros((n_phys * P, rb), np.uint8)
+    for r, pg in zip(*np.nonzero(bt >= 0)):
+        lo, hi = pg * P, min(pg * P + P, max_seq)
+        res[bt[r, pg] * P: bt[r, pg] * P + hi - lo] = c.host_np[0][r, lo:hi]
+    res_d = _dev(res, torch.uint8)
+    base = n_phys * P
+    c.admit(0, _dev(np.arange(R)), _dev(L0))
+    o.admit(0, np.arange(R), L0)
+    for k in range(steps):
+        L = L0 + 1 + k
+        if k == steps // 2:
+            rr, pp = np.nonzero(bt >= 0)
+            pick = rng.choice(rr.size, size=rr.size // 2, replace=False)
+            tr = np.array([(bt[rr[q], pp[q]], rr[q], pp[q], -1) for q in pick], np.int32)
+            c.spill(0, res_d, P, _dev(tr))
+            o.page_copy(0, P, res, tr)
+            for q in pick:
+                bt[rr[q], pp[q]] = -1
+        topk = np.stack([rng.choice(int(x), size=K, replace=False) for x in L]).astype(np.int32)
+        new = rng.integers(0, 256, size=(R, rb), dtype=np.uint8)
+        for r in range(R):        # the forward writes a resident newest page too
+            pg = (L[r] - 1) // P
+            if bt[r, pg] >= 0:
+                res[bt[r, pg] * P + (L[r] - 1) % P] = new[r]
+                res_d[bt[r, pg] * P + (L[r] - 1) % P] = _dev(new[r], torch.uint8)
+        out = torch.empty(R, K, dtype=torch.int32, device="cuda")
+        plan = H.Plan.empty(R, K)
+        c.store_newest(0, _dev(new, torch.uint8), _dev(L))
+        c.swap_in_paged(0, _dev(topk), _dev(L), _dev(bt), P, base, None, out, plan)
+        o.store_newest(0, new, L)
+        eo, ep = o.swap_in_paged(0, topk, L, bt, P, base)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(got, eo), f"step {k}"
+        assert np.array_equal(plan.count.cpu().numpy(), ep.count)
+        view = np.concatenate([res_d.cpu().numpy(), c.hot[0].cpu().numpy().reshape(R * (B + 1), rb)])
+        for r in range(R):
+            for i in range(K):
+                t = topk[r, i]
+                want = new[r] if t == L[r] - 1 else o.host[0][r, t]
+                assert np.array_equal(view[got[r, i]], want), f"step {k} r {r} t {t}"
+        c.backup(0, _dev(L))
+        o.backup(0, L)
+        lru, tok = c.get_state(0)
+        assert np.array_equal(lru.cpu().numpy(), o.lru[0]) and np.array_equal(tok.cpu().numpy(), o.tok[0])
+    torch.cuda.synchronize()
+    assert np.array_equal(c.hot[0].cpu().numpy(), o.hot[0])
+    assert np.array_equal(c.host_np[0], o.host[0])
+    assert c.get_error() == 0
+    c.close()
