@@ -150,3 +150,38 @@ def test_paged_geometries(wl):
 @pytest.mark.timeout(600)
 def test_paged_decode_full():
     _lockstep(W.WORKLOADS["paged_decode"], progress=True, compare_state_every=4)
+
+
+# -- randomized small geometries mixing every feature ------------------------------
+def _random_workload(seed):
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 1500))
+    K = int(rng.integers(1, min(B, 4096) + 1))
+    R = int(rng.integers(1, 9))
+    layers = int(rng.integers(1, 4))
+    anchor_of = [0]
+    for l in range(1, layers):
+        anchor_of.append(l if rng.random() < 0.5 else anchor_of[int(rng.integers(0, l))])
+    anchor_of = tuple(anchor_of[a] if anchor_of[anchor_of[a]] == anchor_of[a] else a for a in anchor_of)
+    paged = rng.random() < 0.4
+    kw = dict(page_size=int(rng.integers(1, 65)), resident_page_frac=float(rng.random())) if paged else \
+        dict(n_resident=int(rng.integers(0, R + 1)) if rng.random() < 0.3 else 0)
+    return W.Workload(f"fuzz{seed}", layers, anchor_of, R=R, B=B, K=K, rb=16 * int(rng.integers(1, 17)),
+                      steps=int(rng.integers(2, 7)), spec=int(rng.integers(1, 4)),
+                      topk_kind="mixture" if rng.random() < 0.7 else "uniform",
+                      seq_first=("uniform", 1, 3 * B + 10), seed=2000 + seed, **kw)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_geometries(seed):
+    wl = _random_workload(seed)
+    blocks = [b for b in (128, 256, 512, 768, 1024) if _launch_shape_fits(wl, b)]
+    block = blocks[seed % len(blocks)]
+    _lockstep(wl, block_size=block, prefetch=bool(seed % 2))
+
+
+def test_buffer_above_8192_slots():
+    # the widest kernel instantiation (16 chunks of 64 slots per wave)
+    wl = W.Workload("wide", 1, (0,), R=2, B=9000, K=3000, rb=16, steps=4, topk_kind="uniform",
+                    seq_first=("list", 12000, 20000), seed=41)
+    _lockstep(wl)
