@@ -47,12 +47,14 @@
  * Errors: a call returns 0, or a negative code: HISPARSE_EINVAL (bad argument
  * seen on the host), HISPARSE_ENOMEM, or HISPARSE_EHIP(e) = -(1000 + e) for a
  * HIP runtime error e.  Host-side checks never read device data.  Broken
- * device-side preconditions (a top-k entry out of range or repeated, L beyond
- * the host pool, a request index out of range, corrupt state, a plan entry
- * out of range) never fault: the affected batch row resolves to all -1 with
- * a plan count of 0, leaves state and buffers untouched, and sets a bit in
- * the device error word (hisparse_get_error).  The fast path and the resident
- * tier address no memory with top-k entries and do not check them.
+ * device-side preconditions never fault; each sets a bit in the device error
+ * word (hisparse_get_error).  In the swap-in calls (a top-k entry out of
+ * range or repeated, L beyond the host pool, a request index out of range,
+ * corrupt state, a bad block-table entry) the affected batch row resolves to
+ * all -1 with a plan count of 0 and leaves state and buffers untouched; the
+ * per-request fast path and resident tier address no memory with top-k
+ * entries and do not check them.  Replay, backup, spill and import skip the
+ * offending row, pair or transfer and carry on with the rest.
  */
 #ifndef HISPARSE_H
 #define HISPARSE_H

@@ -393,3 +393,61 @@ def test_spill_mid_decode_round_trip():
     assert np.array_equal(c.host_np[0], o.host[0])
     assert c.get_error() == 0
     c.close()
+
+
+def test_graph_capture_paged_with_replay():
+    """A paged anchor swap-in, the skip layer's replay and both backups,
+    captured once and replayed step after step against the oracle."""
+    R, B, K, rb, P = 4, 96, 32, 32, 8
+    max_seq = 900
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq, layers=2, anchor_of=(0, 0))
+    o = _oracle_for(c)
+    rng = np.random.default_rng(9)
+    L = rng.integers(150, 700, size=R).astype(np.int32)
+    max_pages = (max_seq + P - 1) // P
+    bt = np.full((R, max_pages), -1, np.int32)
+    sel = rng.choice(R * max_pages, size=R * max_pages // 3, replace=False)
+    bt.reshape(-1)[sel] = rng.permutation(sel.size)
+    base = sel.size * P
+    c.admit(0, _dev(np.arange(R)), _dev(L - 1))
+    o.admit(0, np.arange(R), L - 1)
+    topk_buf = torch.zeros(R, K, dtype=torch.int32, device="cuda")
+    L_buf = torch.zeros(R, dtype=torch.int32, device="cuda")
+    new_buf = torch.zeros(2, R, rb, dtype=torch.uint8, device="cuda")
+    bt_d = _dev(bt)
+    out = torch.zeros(R, K, dtype=torch.int32, device="cuda")
+    plan = H.Plan.empty(R, K)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            c.store_newest(0, new_buf[0], L_buf)
+            c.swap_in_paged(0, topk_buf, L_buf, bt_d, P, base, None, out, plan)
+            c.backup(0, L_buf)
+            c.store_newest(1, new_buf[1], L_buf)
+            c.replay_plan(1, plan)
+            c.backup(1, L_buf)
+    torch.cuda.synchronize()
+    for step in range(8):
+        topk = np.stack([rng.choice(int(x), size=K, replace=False) for x in L]).astype(np.int32)
+        new = rng.integers(0, 256, size=(2, R, rb), dtype=np.uint8)
+        topk_buf.copy_(_dev(topk))
+        L_buf.copy_(_dev(L))
+        new_buf.copy_(_dev(new, torch.uint8))
+        g.replay()
+        _ = (out.sum() + 1).item()
+        o.store_newest(0, new[0], L)
+        eo, ep = o.swap_in_paged(0, topk, L, bt, P, base)
+        o.backup(0, L)
+        o.store_newest(1, new[1], L)
+        o.replay(1, ep)
+        o.backup(1, L)
+        assert np.array_equal(out.cpu().numpy(), eo), f"replay {step}"
+        assert np.array_equal(plan.count.cpu().numpy(), ep.count)
+        L = L + 1
+    for l in range(2):
+        assert np.array_equal(c.hot[l].cpu().numpy(), o.hot[l])
+        assert np.array_equal(c.host_np[l], o.host[l])
+    assert c.get_error() == 0
+    c.close()
