@@ -228,22 +228,26 @@ def main():
     def run(k, timed):
         main = torch.cuda.current_stream(dev)
         if timed:
-            # events bracket each swap-in on the stream it is launched on
-            name = "swap_in_paged" if g.paged else "swap_in"
-            orig = getattr(g.cache, name)
+            # events bracket each resolver launch on the stream it is launched on
+            names = ("swap_in", "store_swap_in", "swap_in_paged")
+            origs = {name: getattr(g.cache, name) for name in names}
 
-            def timed_swap_in(*a, **kw):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(main)
-                orig(*a, **kw)
-                e1.record(main)
-                ev.append((e0, e1))
-            setattr(g.cache, name, timed_swap_in)
+            def timed(fn):
+                def call(*a, **kw):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(main)
+                    fn(*a, **kw)
+                    e1.record(main)
+                    ev.append((e0, e1))
+                return call
+            for name in names:
+                setattr(g.cache, name, timed(origs[name]))
             try:
                 g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=between)
             finally:
-                setattr(g.cache, name, orig)
+                for name in names:
+                    setattr(g.cache, name, origs[name])
         else:
             g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=between)
 

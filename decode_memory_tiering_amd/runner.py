@@ -5,7 +5,8 @@ Hierarchical Sparse Attention", "Decode Workflow" and "Shared-index
 prefetch"; vLLM design note "HiSparse local KV offload architecture",
 "Resident device pages" for the verify rows):
 
-  store_newest(l)                        the forward's KV write
+  store_newest(l)                        the forward's KV write (on an anchor layer
+                                         it rides in the first swap-in's launch)
   anchor layer:  swap_in(l), once per verify row s, each with its own plan row
                  then, with prefetch on, the replays of its skip layers are
                  issued on the side stream after an event
@@ -35,7 +36,7 @@ def prefetch_enabled() -> bool:
 class GpuRun:
     def __init__(self, wl: W.Workload, steps: Optional[int] = None, device: str = "cuda",
                  block_size: int = 0, replay_grid: int = 0, host_flags: int = HISPARSE_HOST_DEFAULT,
-                 prefetch: Optional[bool] = None, fill: bool = True):
+                 prefetch: Optional[bool] = None, fill: bool = True, fuse_store: bool = True):
         import torch
         self.torch = torch
         self.wl = wl
@@ -48,6 +49,8 @@ class GpuRun:
                                    host_flags=host_flags, block_size=block_size,
                                    replay_grid=replay_grid)
         self.prefetch = prefetch_enabled() if prefetch is None else prefetch
+        # an anchor layer's KV write rides in its swap-in launch (store_swap_in)
+        self.fuse_store = fuse_store
         res = W.resident_mask(wl)
         self.resident = torch.from_numpy(res).to(self.dev) if res.any() else None
         self.resident_np = res
@@ -134,7 +137,9 @@ class GpuRun:
         main = torch.cuda.current_stream(self.dev)
         for l in range(wl.num_layers):
             g = wl.anchor_of[l]
-            c.store_newest(l, new_kv[l], seq_lens, self.resident)
+            fused = self.fuse_store and g == l and not self.paged
+            if not fused:
+                c.store_newest(l, new_kv[l], seq_lens, self.resident)
             if self.paged and seq_lens_np is not None:
                 self.store_newest_resident(l, new_kv[l], seq_lens_np)
             if g == l:
@@ -142,6 +147,9 @@ class GpuRun:
                     if self.paged:
                         c.swap_in_paged(l, topk[l][s], seq_lens, self.block_table, wl.page_size,
                                         self.hot_row_base, None, self.out[l][s], plans[l][s])
+                    elif fused and s == 0:
+                        c.store_swap_in(l, new_kv[l], topk[l][s], seq_lens, self.resident, None, self.out[l][s],
+                                        plans[l][s])
                     else:
                         c.swap_in(l, topk[l][s], seq_lens, self.resident, None, self.out[l][s], plans[l][s])
                     if after_swap_in is not None:

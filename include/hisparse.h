@@ -170,6 +170,18 @@ int hisparse_swap_in(hisparse_ctx* ctx, int32_t anchor_layer,
                      const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb,
                      int32_t* out_slots, hisparse_plan plan_row, hipStream_t stream);
 
+/* hisparse_store_newest followed by hisparse_swap_in on the anchor layer,
+ * in one launch: new_rows [nb][rb] (device) is the forward's KV row of each
+ * batch row, written to the newest token's row (L-1 when L <= B, else B;
+ * resident rows skipped) by the resolver's own workgroup.  The resolver
+ * never reads that row and never evicts it, so results are exactly those of
+ * the two calls in sequence, without the second launch ([vLLM]
+ * "Performance invariants": the abstraction adds no kernel launch). */
+int hisparse_store_swap_in(hisparse_ctx* ctx, int32_t anchor_layer, const void* new_rows,
+                           const int32_t* topk_idx, const int32_t* seq_lens,
+                           const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb,
+                           int32_t* out_slots, hisparse_plan plan_row, hipStream_t stream);
+
 /* The same fused resolver with per-page residency ([vLLM] "Resident device
  * pages": resident pages are checked first, then hot rows, then pinned host
  * memory; non-resident pages are host-backed holes).  block_table [nb]

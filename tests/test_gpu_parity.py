@@ -97,6 +97,12 @@ def test_ragged_geometries(wl, block):
     _lockstep(wl, block_size=block)
 
 
+@pytest.mark.parametrize("wl", [W.WORKLOADS["tiny"], RAGGED[0], RAGGED[2]], ids=["tiny", "ragged_a", "ragged_c"])
+def test_separate_store_launch(wl):
+    # the forward's KV write as its own launch instead of inside the swap-in
+    _lockstep(wl, fuse_store=False)
+
+
 def test_fast_to_slow_transition():
     B = 512
     wl = W.Workload("transition", 1, (0,), R=6, B=B, K=128, rb=64, steps=8,
