@@ -275,6 +275,36 @@ def hisparse_version() -> int:
 
 
 # ---------------------------------------------------------------------------
+# the serving config's JSON keys
+# ---------------------------------------------------------------------------
+def parse_hisparse_config(text_or_dict) -> dict:
+    """Keyword arguments for HiSparseCache from the JSON keys of SGLang's
+    --hisparse-config (SGLang guide "HiSparse: Hierarchical Sparse
+    Attention", "HiSparse Config Parameters"): top_k -> K,
+    device_buffer_size -> B, swap_in_block_size -> the swap-in workgroup
+    size (a multiple of 64 in [128, 1024]; the guide's 960 is one).
+    host_to_device_ratio sizes the host pool in a serving system; here the
+    caller sizes it through max_seq, so the key is accepted and ignored."""
+    import json
+    cfg = json.loads(text_or_dict) if isinstance(text_or_dict, str) else dict(text_or_dict)
+    known = {"top_k", "device_buffer_size", "host_to_device_ratio", "swap_in_block_size"}
+    unknown = set(cfg) - known
+    if unknown:
+        raise ValueError(f"unknown hisparse-config keys: {sorted(unknown)}")
+    if "top_k" not in cfg or "device_buffer_size" not in cfg:
+        raise ValueError("hisparse-config needs top_k and device_buffer_size")
+    out = dict(K=int(cfg["top_k"]), B=int(cfg["device_buffer_size"]))
+    bs = int(cfg.get("swap_in_block_size", 0))
+    if bs and (bs % 64 or not 128 <= bs <= 1024):
+        raise ValueError(f"swap_in_block_size {bs}: needs a multiple of 64 in [128, 1024] (wave64)")
+    if bs:
+        out["block_size"] = bs
+    if int(out["K"]) > int(out["B"]):
+        raise ValueError("top_k must not exceed device_buffer_size")
+    return out
+
+
+# ---------------------------------------------------------------------------
 # a cache object: pinned host pools + device hot buffers + a context
 # ---------------------------------------------------------------------------
 def host_array(ptr: int, shape) -> np.ndarray:

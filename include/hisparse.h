@@ -42,7 +42,10 @@
  * back to the host, and may be captured in a HIP graph.  Ownership: the caller
  * owns host pools, hot buffers, inputs, outputs and plan buffers; the library
  * owns only the per-anchor-layer LRU state ([R][B] int32 lru and slot map)
- * and one device error word.
+ * and one device error word.  Calls that use one anchor layer's state
+ * (swap_in, store_swap_in, swap_in_paged, admit, get/set_state) must be
+ * ordered by the caller (one stream, or events); calls on different anchor
+ * layers, and replays of different skip layers, may run concurrently.
  *
  * Errors: a call returns 0, or a negative code: HISPARSE_EINVAL (bad argument
  * seen on the host), HISPARSE_ENOMEM, or HISPARSE_EHIP(e) = -(1000 + e) for a

@@ -75,3 +75,16 @@ def test_null_context_rejected(lib):
     assert lib.hisparse_swap_in(None, 0, None, None, None, None, 1, None, H.hisparse_plan(), None) == -22
     assert lib.hisparse_backup(None, 0, None, None, None, 1, None) == -22
     assert lib.hisparse_replay_plan(None, 0, H.hisparse_plan(), None, 1, None) == -22
+
+
+def test_serving_config_keys():
+    from decode_memory_tiering_amd.hisparse import parse_hisparse_config
+    kw = parse_hisparse_config('{"top_k": 2048, "device_buffer_size": 6144, "host_to_device_ratio": 10, '
+                               '"swap_in_block_size": 960}')
+    assert kw == dict(K=2048, B=6144, block_size=960)
+    assert parse_hisparse_config({"top_k": 8, "device_buffer_size": 16}) == dict(K=8, B=16)
+    for bad in ('{"top_k": 8, "device_buffer_size": 16, "swap_in_block_size": 100}',
+                '{"top_k": 32, "device_buffer_size": 16}', '{"top_k": 8}',
+                '{"top_k": 8, "device_buffer_size": 16, "page": 4}'):
+        with pytest.raises(ValueError):
+            parse_hisparse_config(bad)
