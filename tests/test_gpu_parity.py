@@ -191,3 +191,9 @@ def test_buffer_above_8192_slots():
     wl = W.Workload("wide", 1, (0,), R=2, B=9000, K=3000, rb=16, steps=4, topk_kind="uniform",
                     seq_first=("list", 12000, 20000), seed=41)
     _lockstep(wl)
+
+
+@pytest.mark.parametrize("wl", [W.WORKLOADS["tiny"], RAGGED[0]], ids=["tiny", "ragged_a"])
+def test_block_size_960(wl):
+    # the serving guide's swap_in_block_size: 15 waves, not a power of two
+    _lockstep(wl, block_size=960)
