@@ -10,11 +10,15 @@ before timing; host pools live in pinned host memory, as the method intends.
 
 Prints one JSON line.  `value` = top-k entries resolved per second over the
 timed steps (all layers and verify rows), wall clock between two
-synchronisations.  `roofline` describes the swap-in kernel: its miss copy is
+synchronisations; the median of --runs repetitions of the whole decode, each
+after re-admitting every request, so each repeats the first exactly.  `roofline` describes the swap-in kernel: its miss copy is
 bound by the host link (PCIe 5.0 x16 between the host and the MI355X), so
 achieved = miss bytes per launch / mean launch time, against the link's
 published per-direction rate; the link rate this box measures for a 1 GiB
-pinned host -> HBM copy is reported beside it.
+pinned host -> HBM copy is reported beside it.  The skip layers' plan replay
+and the eager backup get the same per-launch figures (rows moved x row bytes
+/ mean launch time), from events on the stream each runs on in one more run
+of the decode after the timed ones.
 """
 from __future__ import annotations
 
@@ -85,23 +89,54 @@ def counter_traffic(workload):
         return None
 
 
-def cpu_baseline(wl, steps, host_pools, topk_all, newkv_all, budget_s=20.0):
-    """The oracle, as it stands, on the same inputs: single thread, the first
-    steps of the same decode, until about budget_s of oracle time."""
+def cpu_baseline(wl, steps, warmup, host_pools, topk_all, newkv_all, budget_s=10.0, max_threads=16):
+    """The oracle, as it stands, on the same inputs and the same timed steps
+    as the GPU (steps [warmup, steps) of the decode, the warmup steps run
+    untimed): the decode, re-admitted between repetitions, is repeated until
+    about budget_s of oracle time on one thread; then the same again with the
+    requests split over the host's cores, one share per thread (requests are
+    independent and the oracle keeps no global state, so the shares run side
+    by side).  The oracle's hot buffers are written once beforehand, so no
+    timed step pays for first-touch page faults."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle.runner import OracleRun
     o = OracleRun(wl, steps, host_pools=host_pools)
-    t_run, entries, done = 0.0, 0, 0
-    for k in range(steps):
-        t0 = time.perf_counter()
-        o.step(k, topk_all[k], newkv_all[k])
-        t_run += time.perf_counter() - t0
-        entries += sum(int(np.count_nonzero(v >= 0)) for v in topk_all[k].values())
-        done += 1
-        if t_run > budget_s:
-            break
-    return dict(value=entries / t_run, unit="top-k entries resolved/s", cores=1, kind="oracle",
-                sample=f"first {done} of {steps} decode steps of the same workload, all {wl.R} requests "
-                       f"and {wl.num_layers} layer(s), single thread, oracle time {t_run:.2f}s")
+    for h in o.orc.hot:
+        h.fill(0)
+    per_step = [sum(int(np.count_nonzero(v >= 0)) for v in topk_all[k].values()) for k in range(steps)]
+
+    def sweep(call):
+        t_run, entries, done, reps = 0.0, 0, 0, 0
+        while t_run <= budget_s and reps < 1000:
+            o.readmit()
+            reps += 1
+            for k in range(warmup):
+                call(k)
+            for k in range(warmup, steps):
+                t0 = time.perf_counter()
+                call(k)
+                t_run += time.perf_counter() - t0
+                entries += per_step[k]
+                done += 1
+                if t_run > budget_s:
+                    break
+        return t_run, entries, done, reps
+
+    t1, e1, done, reps = sweep(lambda k: o.step(k, topk_all[k], newkv_all[k]))
+    threads = max(1, min(len(os.sched_getaffinity(0)), max_threads, wl.R))
+    shares = [c for c in np.array_split(np.arange(wl.R, dtype=np.int32), threads) if c.size]
+    with ThreadPoolExecutor(len(shares)) as pool:
+        def parallel(k):
+            list(pool.map(lambda req: o.step(k, topk_all[k], newkv_all[k], req), shares))
+        tn, en, done_n, _ = sweep(parallel) if threads > 1 else (t1, e1, done, reps)
+    what = (f"{done} timed decode steps (steps {warmup}..{steps - 1} of the same decode as the GPU run, "
+            f"{reps} repetition(s), re-admitted in between, warmup steps untimed), all {wl.R} requests "
+            f"and {wl.num_layers} layer(s)")
+    return dict(value=e1 / t1, unit="top-k entries resolved/s", cores=1, kind="oracle",
+                sample=f"{what}, single thread, oracle time {t1:.2f}s",
+                threads=dict(value=en / tn, cores=len(shares),
+                             sample=f"{done_n} timed decode steps, requests split over {len(shares)} "
+                                    f"threads, oracle wall time {tn:.2f}s"))
 
 
 def measure_page_copy(dev, W, args):
@@ -155,6 +190,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--runs", type=int, default=5,
+                    help="repetitions of the whole timed decode (re-admitted in between); the median is reported")
     ap.add_argument("--workload", default="fastpath_mix")
     ap.add_argument("--block-size", type=int, default=0)
     ap.add_argument("--replay-grid", type=int, default=0)
@@ -215,7 +252,6 @@ def main():
     torch.cuda.synchronize(dev)
     log(f"[bench] {wl.name}: setup {time.time() - t_setup:.1f}s")
 
-    ev = []   # (start, end) events of every timed swap-in launch
     between = None
     if args.layer_compute_mib:
         n = args.layer_compute_mib << 20
@@ -225,47 +261,77 @@ def main():
         def between(_l):
             cdst.copy_(csrc)
 
-    def run(k, timed):
-        main = torch.cuda.current_stream(dev)
-        if timed:
-            # events bracket each resolver launch on the stream it is launched on
-            names = ("swap_in", "store_swap_in", "swap_in_paged")
-            origs = {name: getattr(g.cache, name) for name in names}
+    # Launch events, by kind, each pair recorded on the stream its launch goes
+    # to.  The timed runs record only the resolver's launches (the roofline's
+    # kernel); one more run after them, outside the reported value, records
+    # the replays and backups as well.  Every event is created before the
+    # first timed step, so none is created inside a timed region.
+    import inspect
+    kinds = {"swap_in": "swap_in", "store_swap_in": "swap_in", "swap_in_paged": "swap_in",
+             "replay_plan": "replay", "backup": "backup"}
+    per_step = {"swap_in": len(wl.anchors) * wl.spec, "replay": len(wl.skip_layers) * wl.spec,
+                "backup": wl.num_layers}
+    n_events = 2 * args.steps * (args.runs * per_step["swap_in"] + sum(per_step.values()))
+    pool = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+    ev = {k: [] for k in per_step}
+    recording = set()
+    origs = {name: getattr(g.cache, name) for name in kinds}
 
-            def timed(fn):
-                def call(*a, **kw):
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(main)
-                    fn(*a, **kw)
-                    e1.record(main)
-                    ev.append((e0, e1))
-                return call
-            for name in names:
-                setattr(g.cache, name, timed(origs[name]))
-            try:
-                g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=between)
-            finally:
-                for name in names:
-                    setattr(g.cache, name, origs[name])
-        else:
-            g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=between)
+    def timed(name, fn):
+        kind = kinds[name]
+        pos = list(inspect.signature(fn).parameters).index("stream")
 
-    for k in range(args.warmup):
-        run(k, False)
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for k in range(args.warmup, total):
-        run(k, True)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
+        def call(*a, **kw):
+            if kind not in recording:
+                return fn(*a, **kw)
+            stream = kw.get("stream") or (a[pos] if len(a) > pos else None) or torch.cuda.current_stream(dev)
+            e0, e1 = pool.pop(), pool.pop()
+            e0.record(stream)
+            fn(*a, **kw)
+            e1.record(stream)
+            ev[kind].append((e0, e1))
+        return call
+
+    def run(k):
+        g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=between)
+
+    # every run re-admits all requests and repeats the same decode exactly:
+    # W untimed warmup steps, then exactly K timed steps between two
+    # synchronisations
+    walls = []
+    for name in kinds:
+        setattr(g.cache, name, timed(name, origs[name]))
+    try:
+        for i in range(args.runs + 1):
+            detail = i == args.runs
+            if i:
+                g.readmit()
+            recording.clear()
+            for k in range(args.warmup):
+                run(k)
+            torch.cuda.synchronize(dev)
+            recording.update(per_step if detail else ("swap_in",))
+            t0 = time.perf_counter()
+            for k in range(args.warmup, total):
+                run(k)
+            torch.cuda.synchronize(dev)
+            if not detail:
+                walls.append(time.perf_counter() - t0)
+                log(f"[bench] run {i}: {walls[-1] * 1e3:.2f} ms")
+    finally:
+        for name in kinds:
+            setattr(g.cache, name, origs[name])
+    wall = float(np.median(walls))
 
     entries = sum(int(np.count_nonzero(v >= 0)) for k in range(args.warmup, total) for v in topk_all[k].values())
+    # plan counts hold the last run's misses; every run has the same ones
     misses = sum(int(p.count.sum().item()) for k in range(args.warmup, total)
                  for a in wl.anchors for p in step_plans[k][a])
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    swap_ev = ev["swap_in"][:per_step["swap_in"] * args.steps * args.runs]   # timed runs only
+    n_swap = len(swap_ev) // args.runs
+    launch_ms = [a.elapsed_time(b) for a, b in swap_ev]
     mean_launch_s = float(np.mean(launch_ms)) * 1e-3
-    miss_bytes_per_launch = misses * wl.rb / len(ev)
+    miss_bytes_per_launch = misses * wl.rb / n_swap
     achieved = miss_bytes_per_launch / mean_launch_s / 1e9
     # resolve-pass metadata bytes per launch (top-k read + slot write per entry;
     # slot map read, LRU read + write per slow row; slot map write + plan pair per miss)
@@ -275,6 +341,21 @@ def main():
         L = W.seq_lens_at(wl, k)
         slow_rows += int(np.count_nonzero((L > wl.B) & (res == 0))) * len(wl.anchors) * wl.spec
     meta_bytes = entries * 8 + slow_rows * 12 * wl.B + misses * 12 + slow_rows * 4
+
+    def kind_stats(kind, rows_per_run):
+        """Host-link rate of one launch kind: rows moved x row bytes / mean launch time."""
+        if not ev[kind]:
+            return None
+        ms = [a.elapsed_time(b) for a, b in ev[kind]]
+        n = len(ev[kind])
+        t = float(np.mean(ms)) * 1e-3
+        return dict(launches=n, mean_launch_us=t * 1e6, rows_per_launch=rows_per_run / n,
+                    gbps=rows_per_run * wl.rb / n / t / 1e9)
+
+    # every skip layer replays each verify row's plan of its anchor
+    replay_rows = sum(int(p.count.sum().item()) for k in range(args.warmup, total)
+                      for x in wl.skip_layers for p in step_plans[k][wl.anchor_of[x]])
+    backup_rows = args.steps * wl.num_layers * int(np.count_nonzero(res == 0))
     err = g.cache.get_error()
     if err:
         log(f"[bench] device error word {err:#x}")
@@ -285,7 +366,7 @@ def main():
     if not args.no_cpu_baseline:
         newkv_np = [t.cpu().numpy() for t in newkv_dev]
         g.close()
-        cpu = cpu_baseline(wl, total, host_copy, topk_all, newkv_np)
+        cpu = cpu_baseline(wl, total, args.warmup, host_copy, topk_all, newkv_np)
     else:
         g.close()
 
@@ -319,16 +400,20 @@ def main():
             "unit": "GB/s",
             "frac": achieved / PCIE5_X16_GBPS,
             "traffic": counter_traffic(wl.name),
-            "launches": len(ev),
+            "launches": n_swap,
             "mean_launch_us": mean_launch_s * 1e6,
             "miss_bytes_per_launch": miss_bytes_per_launch,
             "measured_link_gbps": link,
             "frac_of_measured_link": (achieved / link) if link else None,
-            "resolve_hbm_gbps": meta_bytes / len(ev) / mean_launch_s / 1e9,
-            "resolve_hbm_frac": meta_bytes / len(ev) / mean_launch_s / 1e9 / HBM_PEAK_GBPS,
+            "resolve_hbm_gbps": meta_bytes / n_swap / mean_launch_s / 1e9,
+            "resolve_hbm_frac": meta_bytes / n_swap / mean_launch_s / 1e9 / HBM_PEAK_GBPS,
         },
+        "runs": {"n": args.runs, "ms_per_step": [w / args.steps * 1e3 for w in walls],
+                 "value_min": entries / max(walls), "value_max": entries / min(walls)},
+        "replay": kind_stats("replay", replay_rows),
+        "backup": kind_stats("backup", backup_rows),
         "misses_per_step": misses / args.steps,
-        "kernel_time_frac": float(np.sum(launch_ms)) * 1e-3 / wall,
+        "kernel_time_frac": float(np.sum(launch_ms)) * 1e-3 / args.runs / wall,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -76,11 +76,20 @@ class GpuRun:
 
     # -- set-up ----------------------------------------------------------------
     def fill_and_admit(self):
-        torch, wl = self.torch, self.wl
+        wl = self.wl
         for l in range(wl.num_layers):
             W.fill_host_pool(self.cache.host[l], wl, l, self.L0, self.dev)
         if self.paged:
             self._fill_resident()
+        self.readmit()
+
+    def readmit(self):
+        """Admit every request again on every anchor layer (state reset, and
+        the hot rows of short requests refilled from the host pool).  Host
+        rows past the prefill hold what the previous run's backups wrote,
+        which a new run writes again with the same values, so a run after
+        readmit() repeats the previous one exactly."""
+        torch, wl = self.torch, self.wl
         req = torch.arange(wl.R, dtype=torch.int32, device=self.dev)
         L0 = torch.from_numpy(self.L0.astype(np.int32)).to(self.dev)
         for g in wl.anchors:

@@ -35,8 +35,7 @@ class OracleRun:
             self._fill_cpu()
         self.L0 = W.prompt_lens(wl)
         self.resident = W.resident_mask(wl)
-        for g in wl.anchors:
-            self.orc.admit(g, np.arange(wl.R), self.L0)
+        self.readmit()
         if wl.page_size > 0:
             self.block_table, n_phys = W.block_table(wl, self.steps)
             self.hot_row_base = n_phys * wl.page_size
@@ -47,31 +46,44 @@ class OracleRun:
             t = torch.from_numpy(self.orc.host[l])
             W.fill_host_pool(t, self.wl, l, W.prompt_lens(self.wl), "cpu")
 
-    def step(self, step: int, topk: Dict[int, np.ndarray], new_kv: np.ndarray):
+    def readmit(self):
+        """Admit every request again (state reset; short requests' hot rows
+        refilled from the host pool)."""
+        for g in self.wl.anchors:
+            self.orc.admit(g, np.arange(self.wl.R), self.L0)
+
+    def step(self, step: int, topk: Dict[int, np.ndarray], new_kv: np.ndarray,
+             req: Optional[np.ndarray] = None):
         """topk[g]: [S][R][K]; new_kv: [layers][R][rb].  Returns
-        out[g] ([S][R][K]) and plans[g] (list of S plan rows)."""
+        out[g] ([S][nb][K]) and plans[g] (list of S plan rows).  req: the
+        requests to step (default all R, in order); requests are independent,
+        so disjoint subsets may be stepped from different threads."""
         wl, orc = self.wl, self.orc
         L = W.seq_lens_at(wl, step)
         res = self.resident if self.resident.any() else None
+        sel = slice(None) if req is None else req
+        ridx = None if req is None else np.ascontiguousarray(req, dtype=np.int32)
+        L, res = L[sel], (None if res is None else res[sel])
+        bt = self.block_table[sel] if wl.page_size > 0 else None
         outs: Dict[int, np.ndarray] = {}
         plans: Dict[int, List[Plan]] = {}
         for l in range(wl.num_layers):
             g = wl.anchor_of[l]
-            orc.store_newest(l, new_kv[l], L, res)
+            orc.store_newest(l, new_kv[l][sel], L, res, ridx)
             if g == l:
                 o, p = [], []
                 for s in range(wl.spec):
                     if wl.page_size > 0:
-                        out, plan = orc.swap_in_paged(l, topk[l][s], L, self.block_table, wl.page_size,
-                                                      self.hot_row_base)
+                        out, plan = orc.swap_in_paged(l, topk[l][s][sel], L, bt, wl.page_size,
+                                                      self.hot_row_base, ridx)
                     else:
-                        out, plan = orc.swap_in(l, topk[l][s], L, res)
+                        out, plan = orc.swap_in(l, topk[l][s][sel], L, res, ridx)
                     o.append(out)
                     p.append(plan)
                 outs[l] = np.stack(o)
                 plans[l] = p
             else:
                 for s in range(wl.spec):
-                    orc.replay(l, plans[g][s])
-            orc.backup(l, L, res)
+                    orc.replay(l, plans[g][s], ridx)
+            orc.backup(l, L, res, ridx)
         return outs, plans

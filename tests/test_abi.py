@@ -51,6 +51,8 @@ def test_pure_host_calls(lib):
     dict(top_k=10, device_buffer_size=5),          # K > B
     dict(top_k=0, device_buffer_size=5),
     dict(top_k=8, device_buffer_size=20000),       # B above the supported maximum
+    dict(top_k=8, device_buffer_size=16385),       # one slot above it
+    dict(top_k=4097, device_buffer_size=8192),     # K above the supported maximum
     dict(row_bytes=24),                            # not a multiple of 16
     dict(num_layers=0),
     dict(block_size=100),

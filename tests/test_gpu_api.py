@@ -10,6 +10,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 from decode_memory_tiering_amd import hisparse as H  # noqa: E402
+from decode_memory_tiering_amd import workload as W  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -451,3 +452,47 @@ def test_graph_capture_paged_with_replay():
         assert np.array_equal(c.host_np[l], o.host[l])
     assert c.get_error() == 0
     c.close()
+
+
+@pytest.mark.parametrize("wl", [
+    W.Workload(
+        "rerun_mix", 3, (0, 0, 2), R=7, B=200, K=64, rb=32, steps=6, spec=2, n_resident=2,
+        seq_first=("uniform", 100, 400), seed=11),
+    W.Workload(
+        "rerun_paged", 2, (0, 0), R=6, B=150, K=50, rb=48, steps=5, page_size=16,
+        resident_page_frac=0.3, seq_first=("uniform", 120, 500), seed=12),
+], ids=lambda w: w.name)
+def test_readmit_repeats_the_decode_exactly(wl):
+    """A whole decode run again after every request is admitted again gives
+    the same slots, plans, hot buffers and host pools, bit for bit (the
+    benchmark's repetitions rely on it)."""
+    from decode_memory_tiering_amd.runner import GpuRun, draw_topk, new_kv_all_layers
+    g = GpuRun(wl, wl.steps)
+    streams = {a: W.TopkStream(wl, a) for a in wl.anchors}
+    topk = [{a: _dev(v) for a, v in draw_topk(wl, streams, k).items()} for k in range(wl.steps)]
+    newkv = [new_kv_all_layers(wl, k, "cuda") for k in range(wl.steps)]
+
+    def decode():
+        got = []
+        for k in range(wl.steps):
+            g.step(topk[k], newkv[k], g.seq_lens(k), seq_lens_np=W.seq_lens_at(wl, k))
+            got.append([(g.out[a].cpu().numpy().copy(), [(p.pos.cpu().numpy().copy(), p.slot.cpu().numpy().copy(),
+                                                         p.count.cpu().numpy().copy()) for p in g.plans[a]])
+                        for a in wl.anchors])
+        torch.cuda.synchronize()
+        return got, [h.cpu().numpy() for h in g.cache.hot], [h.copy() for h in g.cache.host_np]
+
+    first = decode()
+    g.readmit()
+    again = decode()
+    for k, (x, y) in enumerate(zip(first[0], again[0])):
+        for (ox, px), (oy, py) in zip(x, y):
+            assert np.array_equal(ox, oy), f"step {k}"
+            for (a1, b1, c1), (a2, b2, c2) in zip(px, py):
+                assert np.array_equal(c1, c2), f"step {k}"
+                for r in range(c1.shape[0]):
+                    assert np.array_equal(a1[r, :c1[r]], a2[r, :c1[r]]) and np.array_equal(b1[r, :c1[r]], b2[r, :c1[r]])
+    for x, y in zip(first[1] + first[2], again[1] + again[2]):
+        assert np.array_equal(x, y)
+    assert g.cache.get_error() == 0
+    g.close()

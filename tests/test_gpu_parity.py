@@ -193,6 +193,13 @@ def test_buffer_above_8192_slots():
     _lockstep(wl)
 
 
+def test_maximum_sizes():
+    # the largest buffer and top-k the library accepts: 16384 slots, 4096 top-k entries
+    wl = W.Workload("max", 1, (0,), R=2, B=16384, K=4096, rb=16, steps=4,
+                    seq_first=("list", 16000, 40000), seed=43)
+    _lockstep(wl)
+
+
 @pytest.mark.parametrize("wl", [W.WORKLOADS["tiny"], RAGGED[0]], ids=["tiny", "ragged_a"])
 def test_block_size_960(wl):
     # the serving guide's swap_in_block_size: 15 waves, not a power of two
