@@ -128,6 +128,43 @@ def counter_traffic(workload):
         return None
 
 
+def tier_shares(wl, topk_all, steps, misses, block_table=None):
+    """How the valid top-k entries of the given steps were served: resident
+    (request or page), fast path (L <= B), newest token's own row, hot-buffer
+    hit, miss.  Misses come from the run's plan counts; the other tiers follow
+    from the inputs alone.  Also the hot-buffer hit rate, hits / (hits +
+    misses), over the entries that reached the hot lookup."""
+    from decode_memory_tiering_amd import workload as W
+    res = W.resident_mask(wl).astype(bool)
+    n = dict(resident=0, fast_path=0, newest=0, hit=0, miss=int(misses))
+    lookup = 0
+    for k in steps:
+        L = W.seq_lens_at(wl, k).astype(np.int64)
+        for v in topk_all[k].values():            # [S][R][K]
+            for s in range(v.shape[0]):
+                x = v[s].astype(np.int64)
+                valid = x >= 0
+                if block_table is not None:
+                    P = wl.page_size
+                    page = np.where(valid, x // P, 0)
+                    inside = page < block_table.shape[1]
+                    phys = np.where(inside, np.take_along_axis(block_table, np.minimum(page, block_table.shape[1] - 1),
+                                                               1), -1)
+                    is_res = valid & (phys >= 0)
+                else:
+                    is_res = valid & res[:, None]
+                fast = valid & ~is_res & (L <= wl.B)[:, None]
+                newest = valid & ~is_res & ~fast & (x == (L - 1)[:, None])
+                n["resident"] += int(is_res.sum())
+                n["fast_path"] += int(fast.sum())
+                n["newest"] += int(newest.sum())
+                lookup += int((valid & ~is_res & ~fast & ~newest).sum())
+    n["hit"] = lookup - n["miss"]
+    total = sum(n.values())
+    return dict(entries=n, shares={k: v / total for k, v in n.items()},
+                hot_hit_rate=(n["hit"] / lookup) if lookup else None)
+
+
 def cpu_baseline(wl, steps, warmup, host_pools, topk_all, newkv_all, budget_s=10.0, max_threads=16):
     """The oracle, as it stands, on the same inputs and the same timed steps
     as the GPU (steps [warmup, steps) of the decode, the warmup steps run
@@ -457,6 +494,8 @@ def main():
                  "value_min": entries / max(walls), "value_max": entries / min(walls)},
         "replay": kind_stats("replay", replay_rows),
         "backup": kind_stats("backup", backup_rows),
+        "tiers": tier_shares(wl, topk_all, range(args.warmup, total), misses,
+                             g.block_table_np if wl.page_size else None),
         "misses_per_step": misses / args.steps,
         "kernel_time_frac": float(np.sum(launch_ms)) * 1e-3 / args.runs / wall,
         "cpu_baseline": cpu,

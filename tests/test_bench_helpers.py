@@ -1,0 +1,54 @@
+"""The benchmark's tier breakdown, checked against what the oracle actually
+returned: every valid top-k entry is counted in exactly one tier, and the
+hot-buffer hits it derives from the inputs and the miss count equal the hits
+in the oracle's outputs."""
+import numpy as np
+import pytest
+
+import bench
+from decode_memory_tiering_amd import workload as W
+from decode_memory_tiering_amd.runner import draw_topk, new_kv_all_layers
+from oracle.runner import OracleRun
+
+CASES = [
+    W.Workload("tiers_mix", 2, (0, 0), R=8, B=200, K=64, rb=32, steps=6, spec=2, n_resident=2,
+               seq_first=("uniform", 100, 400), seed=21),
+    W.Workload("tiers_paged", 1, (0,), R=6, B=150, K=50, rb=48, steps=5, page_size=16,
+               resident_page_frac=0.3, seq_first=("uniform", 120, 500), seed=22),
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_tier_shares_match_oracle_outputs(wl):
+    o = OracleRun(wl)
+    streams = {a: W.TopkStream(wl, a) for a in wl.anchors}
+    topk_all, misses, hits, resident, newest = [], 0, 0, 0, 0
+    res_mask = W.resident_mask(wl).astype(bool)
+    for k in range(wl.steps):
+        topk = draw_topk(wl, streams, k)
+        topk_all.append(topk)
+        outs, plans = o.step(k, topk, new_kv_all_layers(wl, k, "cpu").numpy())
+        L = W.seq_lens_at(wl, k)
+        for a in wl.anchors:
+            for s in range(wl.spec):
+                misses += int(plans[a][s].count.sum())
+                out, x = outs[a][s], topk[a][s]
+                for r in range(wl.R):
+                    if L[r] <= wl.B or (not wl.page_size and res_mask[r]):
+                        continue
+                    v = out[r][x[r] >= 0]
+                    if wl.page_size:
+                        resident += int((v < o.hot_row_base).sum())
+                        v = v[v >= o.hot_row_base] - (o.hot_row_base + r * (wl.B + 1))
+                    newest += int((v == wl.B).sum())
+                    hits += int(((v >= 0) & (v < wl.B)).sum())
+    hits -= misses
+    got = bench.tier_shares(wl, topk_all, range(wl.steps), misses, o.block_table if wl.page_size else None)
+    assert got["entries"]["hit"] == hits
+    assert got["entries"]["newest"] == newest
+    if wl.page_size:
+        # resident-page entries of long rows; short rows' resident entries count there too
+        assert got["entries"]["resident"] >= resident
+    valid = sum(int((v >= 0).sum()) for t in topk_all for v in t.values())
+    assert sum(got["entries"].values()) == valid
+    assert 0 < got["hot_hit_rate"] < 1

@@ -496,3 +496,56 @@ def test_readmit_repeats_the_decode_exactly(wl):
         assert np.array_equal(x, y)
     assert g.cache.get_error() == 0
     g.close()
+
+
+def test_init_checks_memory_kinds():
+    """The host pool must be pinned, device-addressable and 16-byte aligned;
+    the hot buffer must be device memory.  Anything else is EINVAL at init,
+    before any kernel could touch it."""
+    R, B, K, rb, S = 2, 64, 16, 32, 100
+    nbytes = R * S * rb
+    pinned = H.hisparse_host_alloc(nbytes + 16)
+    hot = torch.zeros(R, B + 1, rb, dtype=torch.uint8, device="cuda")
+    dev_pool = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    pageable = np.zeros(nbytes + 64, np.uint8)
+    page_ptr = (pageable.ctypes.data + 15) & ~15
+    base = dict(top_k=K, device_buffer_size=B, num_layers=1, max_requests=R, max_seq_len=S, row_bytes=rb,
+                anchor_of=[0])
+    try:
+        H.hisparse_destroy(H.hisparse_init(host_pool=[pinned], hot_buffer=[hot], **base))
+        for what, hp, hb in (("pageable host pool", page_ptr, hot),
+                             ("misaligned host pool", pinned + 8, hot),
+                             ("host pool in device memory", dev_pool.data_ptr(), hot),
+                             ("hot buffer in host memory", pinned, pinned)):
+            with pytest.raises(H.HisparseError) as e:
+                H.hisparse_init(host_pool=[hp], hot_buffer=[hb], **base)
+            assert e.value.rc == H.HISPARSE_EINVAL, what
+    finally:
+        H.hisparse_host_free(pinned)
+
+
+def test_calls_reject_bad_layers_and_sizes():
+    c = _cache(R=4, B=64, K=16, rb=32, layers=2, anchor_of=(0, 0))
+    t = torch.zeros(2, c.K, dtype=torch.int32, device="cuda")
+    L = torch.full((2,), 10, dtype=torch.int32, device="cuda")
+    plan = H.Plan.empty(2, c.K)
+    rows = torch.zeros(2 * c.rb + 16, dtype=torch.uint8, device="cuda")
+    cases = [
+        lambda: c.swap_in(1, t, L, None, None, t.clone(), plan),            # a skip layer has no state
+        lambda: c.swap_in(2, t, L, None, None, t.clone(), plan),            # no such layer
+        lambda: c.replay_plan(2, plan),
+        lambda: c.backup(-1, L),
+        lambda: c.store_newest(0, rows[8:8 + 2 * c.rb], L),               # new rows not 16-byte aligned
+        lambda: c.admit(1, torch.zeros(1, dtype=torch.int32, device="cuda"),
+                        torch.ones(1, dtype=torch.int32, device="cuda")),  # admission is per anchor
+    ]
+    big = torch.zeros(5, c.K, dtype=torch.int32, device="cuda")           # 5 batch rows > 4 requests
+    cases.append(lambda: c.swap_in(0, big, torch.full((5,), 10, dtype=torch.int32, device="cuda"), None, None,
+                                   big.clone(), H.Plan.empty(5, c.K)))
+    for i, call in enumerate(cases):
+        with pytest.raises(H.HisparseError) as e:
+            call()
+        assert e.value.rc == H.HISPARSE_EINVAL, i
+    torch.cuda.synchronize()
+    assert c.get_error() == 0
+    c.close()
