@@ -39,14 +39,22 @@ constexpr int kMaxK = 4096;
 constexpr int kDefaultBlock = 1024;
 constexpr int kDefaultReplayGrid = 12;   // enough to fill the host link without crowding the fabric (measured)
 // Copy-loop shape: batches of kCopyUnroll 16-byte loads per thread, kCopyBuffers
-// batches in rotation (measured on MI355X; see copy_rows).
+// batches in rotation (measured on MI355X; see copy_rows).  The swap-in's
+// miss copy runs in every slow batch row's workgroup at once (up to one per
+// CU), so it keeps fewer loads in flight per thread than the replay's small
+// grid does: 4 x 2 measured best across the workloads (8 x 2 and 2 x 2 were
+// 0.5-1.5% slower), the replay keeps 8 x 2.
 #ifndef HISPARSE_COPY_UNROLL
 #define HISPARSE_COPY_UNROLL 8
+#endif
+#ifndef HISPARSE_SWAP_IN_COPY_UNROLL
+#define HISPARSE_SWAP_IN_COPY_UNROLL 4
 #endif
 #ifndef HISPARSE_COPY_BUFFERS
 #define HISPARSE_COPY_BUFFERS 2
 #endif
 constexpr int kCopyUnroll = HISPARSE_COPY_UNROLL;
+constexpr int kSwapInCopyUnroll = HISPARSE_SWAP_IN_COPY_UNROLL;
 constexpr int kReplayStage = 2048;   // plan rows staged in LDS per replay block
 constexpr int kCopyBuffers = HISPARSE_COPY_BUFFERS;
 
@@ -66,16 +74,27 @@ __device__ __forceinline__ uint32_t hash_slot(int32_t t, int bits)
     return (static_cast<uint32_t>(t) * 0x9E3779B1u) >> (32 - bits);
 }
 
-// Exclusive prefix sum, in place, of a[0..n) by one wave; returns the total to
-// every lane.
+// Exclusive prefix sum, in place, of a[0..n) by one wave, n <= 4 * 64;
+// returns the total to every lane.  Lane l owns a[4l .. 4l+4) and issues its
+// four reads together (entries past n read a[0] and count as 0): the rest of
+// the workgroup waits at a barrier meanwhile, so this phase is pure latency.
+constexpr int kScanPerLane = 4;
+static_assert(kMaxB / kWave <= kScanPerLane * kWave && kMaxK / kWave <= kScanPerLane * kWave,
+              "one wave scans the per-chunk counts of the largest buffer and top-k row");
+
 __device__ int wave_exclusive_scan(int* a, int n)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int per = (n + kWave - 1) / kWave;
-    const int base = lane * per;
+    const int base = lane * kScanPerLane;
+    int v[kScanPerLane];
+#pragma unroll
+    for (int k = 0; k < kScanPerLane; ++k) v[k] = a[base + k < n ? base + k : 0];
     int own = 0;
-    for (int k = 0; k < per; ++k)
-        if (base + k < n) own += a[base + k];
+#pragma unroll
+    for (int k = 0; k < kScanPerLane; ++k) {
+        if (base + k >= n) v[k] = 0;
+        own += v[k];
+    }
     int incl = own;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -83,12 +102,10 @@ __device__ int wave_exclusive_scan(int* a, int n)
         if (lane >= d) incl += y;
     }
     int run = incl - own;
-    for (int k = 0; k < per; ++k) {
-        if (base + k < n) {
-            int v = a[base + k];
-            a[base + k] = run;
-            run += v;
-        }
+#pragma unroll
+    for (int k = 0; k < kScanPerLane; ++k) {
+        if (base + k < n) a[base + k] = run;
+        run += v[k];
     }
     return __shfl(incl, kWave - 1, kWave);
 }
@@ -352,7 +369,7 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
         lru_own[k] = (kEarlyLru && in) ? lru[x] : 0;
     }
     for (int h = tid; h <= hmask; h += nthr) s.hash[h] = kHashEmpty;
-    for (int x = tid; x < B; x += nthr) s.hit[x] = 0;
+    for (int q = tid; q < (B + 3) / 4; q += nthr) reinterpret_cast<uint32_t*>(s.hit)[q] = 0u;   // padded to 4 bytes
 
     // -- classify the top-k row ------------------------------------------
     uint32_t err = 0;
@@ -571,7 +588,7 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
     uint8_t* dst = a.hot + size_t(r) * (B + 1) * a.rb;
     const int* pt = s.plan_t;
     const int* pv = s.plan_v;
-    copy_rows<kCopyUnroll, kCopyBuffers>(src, dst, M, a.rb, tid, nthr,
+    copy_rows<kSwapInCopyUnroll, kCopyBuffers>(src, dst, M, a.rb, tid, nthr,
                            [pt](int m) { return pt[m]; }, [pv](int m) { return pv[m]; });
 }
 
