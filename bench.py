@@ -275,6 +275,8 @@ def main():
     ap.add_argument("--replay-grid", type=int, default=0)
     ap.add_argument("--host-flags", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fuse-backup", action="store_true",
+                    help="anchor layers' eager backup as a launch of its own (A/B)")
     ap.add_argument("--no-link", action="store_true")
     ap.add_argument("--layer-compute-mib", type=int, default=0,
                     help="stand-in for each layer's other compute: a device copy of this many MiB on the "
@@ -314,7 +316,8 @@ def main():
     total = args.warmup + args.steps
 
     t_setup = time.time()
-    g = GpuRun(wl, total, block_size=args.block_size, replay_grid=args.replay_grid, host_flags=args.host_flags)
+    g = GpuRun(wl, total, block_size=args.block_size, replay_grid=args.replay_grid, host_flags=args.host_flags,
+               fuse_backup=not args.no_fuse_backup)
     host_copy = None if args.no_cpu_baseline else [np.array(a, copy=True) for a in g.cache.host_np]
     streams = {a: W.TopkStream(wl, a) for a in wl.anchors}
     topk_all = [draw_topk(wl, streams, k) for k in range(total)]
@@ -345,7 +348,8 @@ def main():
     # the replays and backups as well.  Every event is created before the
     # first timed step, so none is created inside a timed region.
     import inspect
-    kinds = {"swap_in": "swap_in", "store_swap_in": "swap_in", "swap_in_paged": "swap_in",
+    kinds = {"swap_in": "swap_in", "store_swap_in": "swap_in", "store_swap_in_backup": "swap_in",
+             "swap_in_paged": "swap_in",
              "replay_plan": "replay", "backup": "backup"}
     per_step = {"swap_in": len(wl.anchors) * wl.spec, "replay": len(wl.skip_layers) * wl.spec,
                 "backup": wl.num_layers}
@@ -433,7 +437,9 @@ def main():
     # every skip layer replays each verify row's plan of its anchor
     replay_rows = sum(int(p.count.sum().item()) for k in range(args.warmup, total)
                       for x in wl.skip_layers for p in step_plans[k][wl.anchor_of[x]])
-    backup_rows = args.steps * wl.num_layers * int(np.count_nonzero(res == 0))
+    # a separate backup launch copies one row per non-resident request (anchor
+    # layers' backups ride in their swap-in launch and have no launch of their own)
+    backup_rows = len(ev["backup"]) * int(np.count_nonzero(res == 0))
     err = g.cache.get_error()
     if err:
         log(f"[bench] device error word {err:#x}")
@@ -471,6 +477,8 @@ def main():
             "parallelism": "single GPU (requests are independent)",
             "prefetch": bool(g.prefetch) if wl.skip_layers else None,
             "layer_compute_mib": args.layer_compute_mib,
+            "fused_launches": ("store+swap-in+backup" if g.fuse_backup else "store+swap-in")
+                              if not wl.page_size else "none",
         },
         "roofline": {
             "kernel": "swap_in_kernel",

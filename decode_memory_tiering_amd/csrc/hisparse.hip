@@ -216,6 +216,7 @@ struct SwapInArgs {
     const int32_t* block_table;
     int32_t paged, max_pages, page_size, hot_row_base;
     const uint8_t* new_rows;     // [nb][rb] or null: the forward's KV write fused into this launch
+    uint8_t* backup_host;        // [R][max_seq][rb] or null: with new_rows, the eager backup fused in too
 };
 
 constexpr unsigned long long kHashEmpty = ~0ull;
@@ -292,18 +293,25 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
     const int L = a.seq_lens[b];
 
     // The forward's KV write, when fused into this launch: the newest token's
-    // row goes to row L-1 (L <= B) or B, as store_newest_kernel does.  The
-    // resolver never reads that row and never picks it as a victim, so the
-    // write needs no ordering against the rest of the kernel.
+    // row goes to row L-1 (L <= B) or B, as store_newest_kernel does, and,
+    // with the backup fused in too, to host position L-1, as backup_kernel
+    // would copy it from there.  The resolver never reads that row, never
+    // picks it as a victim and never reads host position L-1 (it resolves to
+    // the newest row), so neither write needs ordering against the rest.
     if (a.new_rows && !(a.resident && a.resident[b])) {
         const int rs = a.req_idx ? a.req_idx[b] : b;
         if (rs >= 0 && rs < a.R && L >= 1) {
             const int row = L <= B ? L - 1 : B;
             const uint8_t* src = a.new_rows + size_t(b) * a.rb;
             uint8_t* dst = a.hot + (size_t(rs) * (B + 1) + row) * a.rb;
-            for (int c = tid; c < (a.rb >> 4); c += nthr)
-                *reinterpret_cast<u32x4*>(dst + (size_t(c) << 4)) =
-                    *reinterpret_cast<const u32x4*>(src + (size_t(c) << 4));
+            uint8_t* bdst = a.backup_host && L <= a.max_seq
+                                ? a.backup_host + (size_t(rs) * a.max_seq + (L - 1)) * a.rb : nullptr;
+            for (int c = tid; c < (a.rb >> 4); c += nthr) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t(c) << 4));
+                *reinterpret_cast<u32x4*>(dst + (size_t(c) << 4)) = v;
+                if (bdst) *reinterpret_cast<u32x4*>(bdst + (size_t(c) << 4)) = v;
+            }
+            if (a.backup_host && L > a.max_seq && tid == 0) atomicOr(a.err, HISPARSE_DERR_SEQ_LEN);
         } else if (tid == 0) {
             atomicOr(a.err, (rs < 0 || rs >= a.R) ? HISPARSE_DERR_REQ_IDX : HISPARSE_DERR_SEQ_LEN);
         }
@@ -1113,7 +1121,8 @@ namespace {
 int launch_swap_in(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_idx, const int32_t* seq_lens,
                    const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb, int32_t* out,
                    hisparse_plan plan_row, const int32_t* block_table, int32_t paged, int32_t max_pages,
-                   int32_t page_size, int32_t hot_row_base, const void* new_rows, hipStream_t stream)
+                   int32_t page_size, int32_t hot_row_base, const void* new_rows, bool backup,
+                   hipStream_t stream)
 {
     if (!c || !is_anchor(c, anchor_layer) || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
     if (nb == 0) return HISPARSE_OK;
@@ -1128,6 +1137,7 @@ int launch_swap_in(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_id
     a.block_table = block_table; a.paged = paged; a.max_pages = max_pages; a.page_size = page_size;
     a.hot_row_base = hot_row_base;
     a.new_rows = static_cast<const uint8_t*>(new_rows);
+    a.backup_host = backup ? const_cast<uint8_t*>(c->host[anchor_layer]) : nullptr;
     void* args[] = {&a};
     return hip_rc(hipLaunchKernel(reinterpret_cast<const void*>(c->swap_in_fn), dim3(nb), dim3(c->block), args,
                                   c->lds, stream));
@@ -1140,7 +1150,7 @@ int hisparse_swap_in(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_
                      hisparse_plan plan_row, hipStream_t stream)
 {
     return launch_swap_in(c, anchor_layer, topk_idx, seq_lens, resident_mask, req_idx, nb, out_slots, plan_row,
-                          nullptr, 0, 0, 1, 0, nullptr, stream);
+                          nullptr, 0, 0, 1, 0, nullptr, false, stream);
 }
 
 int hisparse_store_swap_in(hisparse_ctx* c, int32_t anchor_layer, const void* new_rows, const int32_t* topk_idx,
@@ -1149,7 +1159,17 @@ int hisparse_store_swap_in(hisparse_ctx* c, int32_t anchor_layer, const void* ne
 {
     if (!new_rows || !aligned16(new_rows)) return HISPARSE_EINVAL;
     return launch_swap_in(c, anchor_layer, topk_idx, seq_lens, resident_mask, req_idx, nb, out_slots, plan_row,
-                          nullptr, 0, 0, 1, 0, new_rows, stream);
+                          nullptr, 0, 0, 1, 0, new_rows, false, stream);
+}
+
+int hisparse_store_swap_in_backup(hisparse_ctx* c, int32_t anchor_layer, const void* new_rows,
+                                  const int32_t* topk_idx, const int32_t* seq_lens, const uint8_t* resident_mask,
+                                  const int32_t* req_idx, int32_t nb, int32_t* out_slots, hisparse_plan plan_row,
+                                  hipStream_t stream)
+{
+    if (!new_rows || !aligned16(new_rows)) return HISPARSE_EINVAL;
+    return launch_swap_in(c, anchor_layer, topk_idx, seq_lens, resident_mask, req_idx, nb, out_slots, plan_row,
+                          nullptr, 0, 0, 1, 0, new_rows, true, stream);
 }
 
 int hisparse_swap_in_paged(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_idx, const int32_t* seq_lens,
@@ -1162,7 +1182,7 @@ int hisparse_swap_in_paged(hisparse_ctx* c, int32_t anchor_layer, const int32_t*
     if (static_cast<long long>(hot_row_base) + static_cast<long long>(c->R) * (c->B + 1) > INT_MAX)
         return HISPARSE_EINVAL;
     return launch_swap_in(c, anchor_layer, topk_idx, seq_lens, nullptr, req_idx, nb, out_rows, plan_row,
-                          block_table, 1, max_pages, page_size, hot_row_base, nullptr, stream);
+                          block_table, 1, max_pages, page_size, hot_row_base, nullptr, false, stream);
 }
 
 int hisparse_replay_plan(hisparse_ctx* c, int32_t skip_layer, hisparse_plan plan_row, const int32_t* req_idx,

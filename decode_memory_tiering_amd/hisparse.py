@@ -36,7 +36,8 @@ HISPARSE_HOST_NONCOHERENT = 2
 # every entry point include/hisparse.h declares
 EXPORTS = (
     "hisparse_init", "hisparse_destroy", "hisparse_admit", "hisparse_store_newest",
-    "hisparse_swap_in", "hisparse_store_swap_in", "hisparse_swap_in_paged", "hisparse_replay_plan", "hisparse_backup", "hisparse_spill", "hisparse_import", "hisparse_get_state",
+    "hisparse_swap_in", "hisparse_store_swap_in", "hisparse_store_swap_in_backup", "hisparse_swap_in_paged",
+    "hisparse_replay_plan", "hisparse_backup", "hisparse_spill", "hisparse_import", "hisparse_get_state",
     "hisparse_set_state", "hisparse_get_error", "hisparse_host_alloc", "hisparse_host_free",
     "hisparse_swap_in_lds_bytes", "hisparse_strerror", "hisparse_version",
 )
@@ -92,6 +93,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hisparse_store_newest.argtypes = [P, I32, P, P, P, P, I32, P]
     lib.hisparse_swap_in.argtypes = [P, I32, P, P, P, P, I32, P, hisparse_plan, P]
     lib.hisparse_store_swap_in.argtypes = [P, I32, P, P, P, P, P, I32, P, hisparse_plan, P]
+    lib.hisparse_store_swap_in_backup.argtypes = [P, I32, P, P, P, P, P, I32, P, hisparse_plan, P]
     lib.hisparse_swap_in_paged.argtypes = [P, I32, P, P, P, I32, I32, I32, P, I32, P, hisparse_plan, P]
     lib.hisparse_replay_plan.argtypes = [P, I32, hisparse_plan, P, I32, P]
     lib.hisparse_backup.argtypes = [P, I32, P, P, P, I32, P]
@@ -212,6 +214,14 @@ def hisparse_store_swap_in(ctx: int, anchor_layer: int, new_rows, topk_idx, seq_
     _check(_lib().hisparse_store_swap_in(ctx, anchor_layer, _ptr(new_rows), _ptr(topk_idx), _ptr(seq_lens),
                                          _ptr(resident_mask), _ptr(req_idx), int(topk_idx.shape[0]),
                                          _ptr(out_slots), plan.c(), _stream(stream)), "hisparse_store_swap_in")
+
+
+def hisparse_store_swap_in_backup(ctx: int, anchor_layer: int, new_rows, topk_idx, seq_lens, resident_mask,
+                                  req_idx, out_slots, plan: Plan, stream=None) -> None:
+    _check(_lib().hisparse_store_swap_in_backup(ctx, anchor_layer, _ptr(new_rows), _ptr(topk_idx), _ptr(seq_lens),
+                                                _ptr(resident_mask), _ptr(req_idx), int(topk_idx.shape[0]),
+                                                _ptr(out_slots), plan.c(), _stream(stream)),
+           "hisparse_store_swap_in_backup")
 
 
 def hisparse_swap_in_paged(ctx: int, anchor_layer: int, topk_idx, seq_lens, block_table, page_size: int,
@@ -369,6 +379,11 @@ class HiSparseCache:
                       stream=None):
         hisparse_store_swap_in(self.ctx, anchor, new_rows, topk_idx, seq_lens, resident_mask, req_idx, out_slots,
                                plan, stream)
+
+    def store_swap_in_backup(self, anchor, new_rows, topk_idx, seq_lens, resident_mask, req_idx, out_slots, plan,
+                             stream=None):
+        hisparse_store_swap_in_backup(self.ctx, anchor, new_rows, topk_idx, seq_lens, resident_mask, req_idx,
+                                      out_slots, plan, stream)
 
     def swap_in_paged(self, anchor, topk_idx, seq_lens, block_table, page_size, hot_row_base, req_idx, out_rows,
                       plan, stream=None):

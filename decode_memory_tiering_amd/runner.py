@@ -11,7 +11,8 @@ prefetch"; vLLM design note "HiSparse local KV offload architecture",
                  then, with prefetch on, the replays of its skip layers are
                  issued on the side stream after an event
   skip layer:    wait for its replay (prefetch) or replay inline
-  backup(l)                              eager backup of the newest token
+  backup(l)                              eager backup of the newest token (on an
+                                         anchor layer it rides in that launch too)
 
 Every launch goes through the C ABI; this module only allocates tensors,
 moves seeded inputs to the device and orders streams.
@@ -36,7 +37,8 @@ def prefetch_enabled() -> bool:
 class GpuRun:
     def __init__(self, wl: W.Workload, steps: Optional[int] = None, device: str = "cuda",
                  block_size: int = 0, replay_grid: int = 0, host_flags: int = HISPARSE_HOST_DEFAULT,
-                 prefetch: Optional[bool] = None, fill: bool = True, fuse_store: bool = True):
+                 prefetch: Optional[bool] = None, fill: bool = True, fuse_store: bool = True,
+                 fuse_backup: bool = True):
         import torch
         self.torch = torch
         self.wl = wl
@@ -49,8 +51,10 @@ class GpuRun:
                                    host_flags=host_flags, block_size=block_size,
                                    replay_grid=replay_grid)
         self.prefetch = prefetch_enabled() if prefetch is None else prefetch
-        # an anchor layer's KV write rides in its swap-in launch (store_swap_in)
+        # an anchor layer's KV write rides in its swap-in launch
+        # (store_swap_in), and so does its eager backup (store_swap_in_backup)
         self.fuse_store = fuse_store
+        self.fuse_backup = fuse_store and fuse_backup
         res = W.resident_mask(wl)
         self.resident = torch.from_numpy(res).to(self.dev) if res.any() else None
         self.resident_np = res
@@ -157,8 +161,8 @@ class GpuRun:
                         c.swap_in_paged(l, topk[l][s], seq_lens, self.block_table, wl.page_size,
                                         self.hot_row_base, None, self.out[l][s], plans[l][s])
                     elif fused and s == 0:
-                        c.store_swap_in(l, new_kv[l], topk[l][s], seq_lens, self.resident, None, self.out[l][s],
-                                        plans[l][s])
+                        fn = c.store_swap_in_backup if self.fuse_backup else c.store_swap_in
+                        fn(l, new_kv[l], topk[l][s], seq_lens, self.resident, None, self.out[l][s], plans[l][s])
                     else:
                         c.swap_in(l, topk[l][s], seq_lens, self.resident, None, self.out[l][s], plans[l][s])
                     if after_swap_in is not None:
@@ -181,7 +185,8 @@ class GpuRun:
                 else:
                     for s in range(wl.spec):
                         c.replay_plan(l, plans[g][s], None, main)
-            c.backup(l, seq_lens, self.resident)
+            if not (fused and self.fuse_backup):
+                c.backup(l, seq_lens, self.resident)
             if between_layers is not None:
                 between_layers(l)
 

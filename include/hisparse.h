@@ -185,6 +185,24 @@ int hisparse_store_swap_in(hisparse_ctx* ctx, int32_t anchor_layer, const void* 
                            const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb,
                            int32_t* out_slots, hisparse_plan plan_row, hipStream_t stream);
 
+/* hisparse_store_newest, hisparse_swap_in and hisparse_backup on the anchor
+ * layer, in one launch: as hisparse_store_swap_in, and each new row also goes
+ * straight to host[anchor][r][L-1] (resident rows skipped; a row with
+ * L > max_seq_len is not backed up and sets HISPARSE_DERR_SEQ_LEN, as
+ * hisparse_backup does).  That is the byte the backup would copy from the
+ * newest row, and no swap-in of this call reads host position L-1 (it
+ * resolves to the newest row), so results are exactly those of the three
+ * calls in sequence.  The host write leaves over the link's device-to-host
+ * direction while the misses arrive over the other.  Use it for the first
+ * verify row of an anchor layer (later verify rows: hisparse_swap_in); skip
+ * layers still call hisparse_backup after their replay.  [SGL] "Decode
+ * Workflow" (forward, swap-in, eager backup); [vLLM] "Performance
+ * invariants" (no extra launch). */
+int hisparse_store_swap_in_backup(hisparse_ctx* ctx, int32_t anchor_layer, const void* new_rows,
+                                  const int32_t* topk_idx, const int32_t* seq_lens,
+                                  const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb,
+                                  int32_t* out_slots, hisparse_plan plan_row, hipStream_t stream);
+
 /* The same fused resolver with per-page residency ([vLLM] "Resident device
  * pages": resident pages are checked first, then hot rows, then pinned host
  * memory; non-resident pages are host-backed holes).  block_table [nb]

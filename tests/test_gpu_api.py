@@ -549,3 +549,35 @@ def test_calls_reject_bad_layers_and_sizes():
     torch.cuda.synchronize()
     assert c.get_error() == 0
     c.close()
+
+
+def test_fused_backup_matches_separate_calls_and_skips_rows_past_the_pool():
+    """store_swap_in_backup == store_newest + swap_in + backup, including a
+    fast-path row whose L exceeds the host pool (no backup, SEQ_LEN flag) and
+    a resident row (neither store nor backup)."""
+    R, B, K, rb, max_seq = 4, 64, 16, 32, 60
+    L = np.array([30, 62, 50, 40], np.int32)            # row 1: L > max_seq (fast path, L <= B)
+    res = np.array([0, 0, 0, 1], np.uint8)               # row 3 resident
+    rng = np.random.default_rng(9)
+    topk = np.stack([rng.choice(int(min(x, max_seq)), size=K, replace=False) for x in L]).astype(np.int32)
+    new = rng.integers(0, 256, size=(R, rb), dtype=np.uint8)
+    results = []
+    for fused in (True, False):
+        c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
+        c.admit(0, _dev(np.arange(R)), _dev(np.minimum(L - 1, max_seq)))
+        out = torch.empty(R, K, dtype=torch.int32, device="cuda")
+        plan = H.Plan.empty(R, K)
+        if fused:
+            c.store_swap_in_backup(0, _dev(new, torch.uint8), _dev(topk), _dev(L), _dev(res, torch.uint8), None,
+                                   out, plan)
+        else:
+            c.store_newest(0, _dev(new, torch.uint8), _dev(L), _dev(res, torch.uint8))
+            c.swap_in(0, _dev(topk), _dev(L), _dev(res, torch.uint8), None, out, plan)
+            c.backup(0, _dev(L), _dev(res, torch.uint8))
+        torch.cuda.synchronize()
+        results.append((out.cpu().numpy(), c.hot[0].cpu().numpy(), c.host_np[0].copy(), c.get_error()))
+        c.close()
+    (o1, hot1, host1, e1), (o2, hot2, host2, e2) = results
+    assert np.array_equal(o1, o2) and np.array_equal(hot1, hot2) and np.array_equal(host1, host2)
+    assert e1 == e2 == H.HISPARSE_DERR_SEQ_LEN
+    assert np.array_equal(host1[0, L[0] - 1], new[0]) and np.array_equal(host1[2, L[2] - 1], new[2])

@@ -97,10 +97,12 @@ def test_ragged_geometries(wl, block):
     _lockstep(wl, block_size=block)
 
 
+@pytest.mark.parametrize("fuse", ["none", "store"])
 @pytest.mark.parametrize("wl", [W.WORKLOADS["tiny"], RAGGED[0], RAGGED[2]], ids=["tiny", "ragged_a", "ragged_c"])
-def test_separate_store_launch(wl):
-    # the forward's KV write as its own launch instead of inside the swap-in
-    _lockstep(wl, fuse_store=False)
+def test_separate_store_and_backup_launches(wl, fuse):
+    # the forward's KV write and the eager backup as launches of their own
+    # ("none"), or only the backup ("store": store_swap_in + backup)
+    _lockstep(wl, fuse_store=fuse == "store", fuse_backup=False)
 
 
 def test_fast_to_slow_transition():
