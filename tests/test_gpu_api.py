@@ -177,11 +177,12 @@ def test_replay_rejects_bad_plan_entries():
     c.close()
 
 
-def test_graph_capture_and_replay():
-    """store_newest + swap_in + backup captured once in a HIP graph, replayed
-    step after step with new inputs copied into the captured buffers (eager
-    work and synchronisation between replays); every replay must equal the
-    oracle's step."""
+@pytest.mark.parametrize("form", ["separate", "fused"])
+def test_graph_capture_and_replay(form):
+    """store_newest + swap_in + backup (three launches, or the one fused
+    launch) captured once in a HIP graph, replayed step after step with new
+    inputs copied into the captured buffers (eager work and synchronisation
+    between replays); every replay must equal the oracle's step."""
     R, B, K, rb = 6, 128, 40, 48
     max_seq = 1200
     c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
@@ -200,9 +201,12 @@ def test_graph_capture_and_replay():
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            c.store_newest(0, new_buf, L_buf)
-            c.swap_in(0, topk_buf, L_buf, None, None, out, plan)
-            c.backup(0, L_buf)
+            if form == "fused":
+                c.store_swap_in_backup(0, new_buf, topk_buf, L_buf, None, None, out, plan)
+            else:
+                c.store_newest(0, new_buf, L_buf)
+                c.swap_in(0, topk_buf, L_buf, None, None, out, plan)
+                c.backup(0, L_buf)
     torch.cuda.synchronize()
     for step in range(10):
         topk = np.stack([rng.choice(int(x), size=K, replace=False) for x in L]).astype(np.int32)
