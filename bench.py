@@ -11,7 +11,10 @@ before timing; host pools live in pinned host memory, as the method intends.
 Prints one JSON line.  `value` = top-k entries resolved per second over the
 timed steps (all layers and verify rows), wall clock between two
 synchronisations; the median of --runs repetitions of the whole decode, each
-after re-admitting every request, so each repeats the first exactly.  `roofline` describes the swap-in kernel: its miss copy is
+after re-admitting every request, so each repeats the first exactly.  The
+resolver's launch durations come from HIP events recorded in the timed runs,
+spread over them so that each step's launches are timed in exactly one run
+(a timed launch costs its step about 7 us of event overhead).  `roofline` describes the swap-in kernel: its miss copy is
 bound by the host link (PCIe 5.0 x16 between the host and the MI355X), so
 achieved = miss bytes per launch / mean launch time, against the link's
 published per-direction rate; the link rate this machine measures is
@@ -342,21 +345,26 @@ def main():
         def between(_l):
             cdst.copy_(csrc)
 
-    # Launch events, by kind, each pair recorded on the stream its launch goes
-    # to.  The timed runs record only the resolver's launches (the roofline's
-    # kernel); one more run after them, outside the reported value, records
-    # the replays and backups as well.  Every event is created before the
-    # first timed step, so none is created inside a timed region.
+    # Launch events, each pair recorded on the stream its launch goes to.  A
+    # timed pair costs the step about 7 us on C2 (the event's barrier keeps
+    # the next launch from overlapping the previous one's tail), so the timed
+    # runs share the work: run i records the resolver's launches of the
+    # steps s with (s - warmup) % runs == i, and over all runs every step's
+    # launches are recorded exactly once.  One more run after them, outside
+    # the reported value, records every replay and backup launch.  Every
+    # event is created before the first timed step.
     import inspect
     kinds = {"swap_in": "swap_in", "store_swap_in": "swap_in", "store_swap_in_backup": "swap_in",
              "swap_in_paged": "swap_in",
              "replay_plan": "replay", "backup": "backup"}
     per_step = {"swap_in": len(wl.anchors) * wl.spec, "replay": len(wl.skip_layers) * wl.spec,
                 "backup": wl.num_layers}
-    n_events = 2 * args.steps * (args.runs * per_step["swap_in"] + sum(per_step.values()))
+    n_events = 2 * args.steps * (per_step["swap_in"] + sum(per_step.values()))
     pool = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
-    ev = {k: [] for k in per_step}
+    ev = {k: [] for k in per_step}      # the extra run's launches, by kind
+    ev_timed = []                       # the timed runs' resolver launches
     recording = set()
+    sink = {"timed": False}
     origs = {name: getattr(g.cache, name) for name in kinds}
 
     def timed(name, fn):
@@ -371,7 +379,7 @@ def main():
             e0.record(stream)
             fn(*a, **kw)
             e1.record(stream)
-            ev[kind].append((e0, e1))
+            (ev_timed if sink["timed"] else ev[kind]).append((e0, e1))
         return call
 
     def run(k):
@@ -392,9 +400,15 @@ def main():
             for k in range(args.warmup):
                 run(k)
             torch.cuda.synchronize(dev)
-            recording.update(per_step if detail else ("swap_in",))
+            sink["timed"] = not detail
+            if detail:
+                recording.update(per_step)
             t0 = time.perf_counter()
             for k in range(args.warmup, total):
+                if not detail:
+                    recording.clear()
+                    if (k - args.warmup) % args.runs == i:
+                        recording.add("swap_in")
                 run(k)
             torch.cuda.synchronize(dev)
             if not detail:
@@ -409,9 +423,9 @@ def main():
     # plan counts hold the last run's misses; every run has the same ones
     misses = sum(int(p.count.sum().item()) for k in range(args.warmup, total)
                  for a in wl.anchors for p in step_plans[k][a])
-    swap_ev = ev["swap_in"][:per_step["swap_in"] * args.steps * args.runs]   # timed runs only
-    n_swap = len(swap_ev) // args.runs
-    launch_ms = [a.elapsed_time(b) for a, b in swap_ev]
+    n_swap = len(ev_timed)              # every resolver launch of one decode, once
+    assert n_swap == per_step["swap_in"] * args.steps, (n_swap, per_step["swap_in"] * args.steps)
+    launch_ms = [a.elapsed_time(b) for a, b in ev_timed]
     mean_launch_s = float(np.mean(launch_ms)) * 1e-3
     miss_bytes_per_launch = misses * wl.rb / n_swap
     achieved = miss_bytes_per_launch / mean_launch_s / 1e9
@@ -505,7 +519,6 @@ def main():
         "tiers": tier_shares(wl, topk_all, range(args.warmup, total), misses,
                              g.block_table_np if wl.page_size else None),
         "misses_per_step": misses / args.steps,
-        "kernel_time_frac": float(np.sum(launch_ms)) * 1e-3 / args.runs / wall,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
