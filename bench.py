@@ -108,11 +108,12 @@ def measure_zero_copy(dev, R=128, rows=4096, rb=1152, grids=(256, 512, 1024)):
     return best
 
 
-def counter_traffic(workload):
-    """HBM + host-link bytes per swap-in launch from the committed rocprofv3
-    counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or
-    None when there is none for this workload or the kernel source changed
-    since the counters were taken."""
+def counter_bytes(workload):
+    """(fetched, written) bytes per swap-in launch from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain
+    copy), or None when there is none for this workload or the kernel source
+    changed since the counters were taken.  Fetched bytes are the host-link
+    reads of the miss rows plus the HBM metadata reads."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"swap_in_kernel_{workload}_counters.md")
     src = os.path.join(ROOT, "decode_memory_tiering_amd", "csrc", "hisparse.hip")
@@ -126,9 +127,15 @@ def counter_traffic(workload):
     if kv.get("src_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
         return None
     try:
-        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+        return float(kv["fetch_bytes_per_launch"]), float(kv["write_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def counter_traffic(workload):
+    """Fetched + written bytes per swap-in launch (see counter_bytes), or None."""
+    fw = counter_bytes(workload)
+    return None if fw is None else fw[0] + fw[1]
 
 
 def tier_shares(wl, topk_all, steps, misses, block_table=None):
@@ -502,6 +509,10 @@ def main():
             "unit": "GB/s",
             "frac": achieved / PCIE5_X16_GBPS,
             "traffic": counter_traffic(wl.name),
+            # the counters' fetched bytes over the live mean launch time: the
+            # miss copy's read rate as the fabric saw it (metadata included)
+            "counter_fetch_gbps": (counter_bytes(wl.name)[0] / mean_launch_s / 1e9)
+                                  if counter_bytes(wl.name) else None,
             "launches": n_swap,
             "mean_launch_us": mean_launch_s * 1e6,
             "miss_bytes_per_launch": miss_bytes_per_launch,
