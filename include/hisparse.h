@@ -37,15 +37,19 @@
  *                          B for the newest position L-1; -1 for padding.
  *
  * Every pointer argument of the hot calls (store_newest, swap_in,
- * replay_plan, backup) is device memory unless stated; all four are
+ * store_swap_in, store_swap_in_backup, swap_in_paged, replay_plan, backup,
+ * spill, import) is device memory unless stated; all of them are
  * asynchronous on the given stream, allocate nothing, never read device data
  * back to the host, and may be captured in a HIP graph.  Ownership: the caller
  * owns host pools, hot buffers, inputs, outputs and plan buffers; the library
  * owns only the per-anchor-layer LRU state ([R][B] int32 lru and slot map)
  * and one device error word.  Calls that use one anchor layer's state
- * (swap_in, store_swap_in, swap_in_paged, admit, get/set_state) must be
- * ordered by the caller (one stream, or events); calls on different anchor
- * layers, and replays of different skip layers, may run concurrently.
+ * (swap_in, store_swap_in, store_swap_in_backup, swap_in_paged, admit,
+ * get/set_state) must be ordered by the caller (one stream, or events), and
+ * so must a call that writes a layer's host pool (backup,
+ * store_swap_in_backup, spill, import) and a later one that may read the
+ * rows it wrote; calls on different anchor layers, and replays of different
+ * skip layers, may run concurrently.
  *
  * Errors: a call returns 0, or a negative code: HISPARSE_EINVAL (bad argument
  * seen on the host), HISPARSE_ENOMEM, or HISPARSE_EHIP(e) = -(1000 + e) for a
