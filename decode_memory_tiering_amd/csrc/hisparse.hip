@@ -127,21 +127,35 @@ struct KeepAll {
 };
 
 template <int U, int NB, typename SrcRow, typename DstRow, typename Keep = KeepAll>
-__device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                          int rows, int rb, int tid, int nthr,
-                                          SrcRow src_row, DstRow dst_row, Keep keep = Keep())
-{
-    const int cpr = rb >> 4;
-    const int total = rows * cpr;
-    if (tid >= total) return;
-    const int drow = nthr / cpr, dcol = nthr - drow * cpr;
-    const int last = rows - 1;
-    int row = tid / cpr, col = tid - row * cpr;   // position of the next chunk to load
-    int c = tid;                                  // its flat index
-
+struct RowCopy {
+    const uint8_t* src;
+    uint8_t* dst;
+    int rb, nthr, cpr, total, drow, dcol, last;
+    int row, col, c;                              // position and flat index of the next chunk to load
+    bool idle;                                    // this thread has no chunk
+    SrcRow src_row;
+    DstRow dst_row;
+    Keep keep;
     u32x4 v[NB][U];
     int vr[NB][U], vc[NB][U];
-    auto load_batch = [&](int p) {
+
+    __device__ __forceinline__ RowCopy(const uint8_t* src_, uint8_t* dst_, int rows, int rb_, int tid, int nthr_,
+                                       SrcRow sr, DstRow dr, Keep kp)
+        : src(src_), dst(dst_), rb(rb_), nthr(nthr_), src_row(sr), dst_row(dr), keep(kp)
+    {
+        cpr = rb >> 4;
+        total = rows * cpr;
+        idle = tid >= total;
+        drow = nthr / cpr;
+        dcol = nthr - drow * cpr;
+        last = rows - 1;
+        row = tid / cpr;
+        col = tid - row * cpr;
+        c = tid;
+    }
+
+    __device__ __forceinline__ void load_batch(int p)
+    {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool in = c < total;
@@ -155,27 +169,59 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8
             row += drow;
             if (col >= cpr) { col -= cpr; ++row; }
         }
-    };
-    auto store_batch = [&](int p, int base) {
+    }
+
+    __device__ __forceinline__ void store_batch(int p, int base)
+    {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (base + u * nthr < total && keep(vr[p][u]))
                 *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(dst_row(vr[p][u])) * rb +
                                           (static_cast<size_t>(vc[p][u]) << 4)) = v[p][u];
         }
-    };
+    }
 
+    // Issue the loads of the first NB-1 batches.  Only src_row is used, so
+    // this may run before the destination rows are known.
+    __device__ __forceinline__ void prime()
+    {
+        if (idle) return;
 #pragma unroll
-    for (int p = 0; p < NB - 1; ++p) load_batch(p);
-    for (int base = tid;;) {
+        for (int p = 0; p < NB - 1; ++p) load_batch(p);
+    }
+
+    // The rest of the copy; dst_row must be valid from here on.
+    __device__ __forceinline__ void finish(int tid)
+    {
+        if (idle) return;
+        for (int base = tid;;) {
 #pragma unroll
-        for (int p = 0; p < NB; ++p) {
-            load_batch((p + NB - 1) % NB);
-            store_batch(p, base);
-            base += U * nthr;
-            if (base >= total) return;
+            for (int p = 0; p < NB; ++p) {
+                load_batch((p + NB - 1) % NB);
+                store_batch(p, base);
+                base += U * nthr;
+                if (base >= total) return;
+            }
         }
     }
+};
+
+template <int U, int NB, typename SrcRow, typename DstRow, typename Keep = KeepAll>
+__device__ __forceinline__ RowCopy<U, NB, SrcRow, DstRow, Keep>
+make_row_copy(const uint8_t* src, uint8_t* dst, int rows, int rb, int tid, int nthr, SrcRow src_row, DstRow dst_row,
+              Keep keep = Keep())
+{
+    return RowCopy<U, NB, SrcRow, DstRow, Keep>(src, dst, rows, rb, tid, nthr, src_row, dst_row, keep);
+}
+
+template <int U, int NB, typename SrcRow, typename DstRow, typename Keep = KeepAll>
+__device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                          int rows, int rb, int tid, int nthr,
+                                          SrcRow src_row, DstRow dst_row, Keep keep = Keep())
+{
+    auto cp = make_row_copy<U, NB>(src, dst, rows, rb, tid, nthr, src_row, dst_row, keep);
+    cp.prime();
+    cp.finish(tid);
 }
 
 // Replay's variant: row m goes from host row src_row[m] to hot row
@@ -536,6 +582,32 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
         return;
     }
 
+    // -- miss positions, then the first copy loads ---------------------------
+    // The m-th miss reads host row plan_t[m]; that is known as soon as the
+    // miss ranks are, so the first batch of the copy's loads is issued here
+    // and is in flight while the LRU list is reordered and the victims are
+    // chosen (the copy's stores wait for those).
+    int m_own[EK];
+#pragma unroll
+    for (int k = 0; k < EK; ++k) {
+        const int c = k * nwaves + wave;
+        m_own[k] = -1;
+        if (c < nck && ((mbits >> k) & 1u)) {
+            const int m = s.cnt_k[c] + lp_k[k];
+            s.plan_t[m] = t_own[k];
+            m_own[k] = m;
+        }
+    }
+    __syncthreads();
+    const uint8_t* src = a.host + size_t(r) * a.max_seq * a.rb;
+    uint8_t* dst = a.hot + size_t(r) * (B + 1) * a.rb;
+    const int* pt = s.plan_t;
+    const int* pv = s.plan_v;
+    auto copy = make_row_copy<kSwapInCopyUnroll, kCopyBuffers>(src, dst, M, a.rb, tid, nthr,
+                                                               [pt](int m) { return pt[m]; },
+                                                               [pv](int m) { return pv[m]; });
+    copy.prime();
+
     // -- LRU reorder and victim choice ------------------------------------
     // new order: non-hit slots n >= M, then hit slots, then victims n < M.
 #pragma unroll
@@ -557,17 +629,6 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
                 }
             }
             lru[pos] = x;
-        }
-    }
-    int m_own[EK];
-#pragma unroll
-    for (int k = 0; k < EK; ++k) {
-        const int c = k * nwaves + wave;
-        m_own[k] = -1;
-        if (c < nck && ((mbits >> k) & 1u)) {
-            const int m = s.cnt_k[c] + lp_k[k];
-            s.plan_t[m] = t_own[k];
-            m_own[k] = m;
         }
     }
     __syncthreads();
@@ -592,12 +653,7 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
     if (tid == 0) a.plan_count[b] = M;
 
     // -- miss copy: pinned host rows -> victim slots -----------------------
-    const uint8_t* src = a.host + size_t(r) * a.max_seq * a.rb;
-    uint8_t* dst = a.hot + size_t(r) * (B + 1) * a.rb;
-    const int* pt = s.plan_t;
-    const int* pv = s.plan_v;
-    copy_rows<kSwapInCopyUnroll, kCopyBuffers>(src, dst, M, a.rb, tid, nthr,
-                           [pt](int m) { return pt[m]; }, [pv](int m) { return pv[m]; });
+    copy.finish(tid);
 }
 
 // ---------------------------------------------------------------------------
