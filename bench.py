@@ -362,7 +362,7 @@ def main():
     # event is created before the first timed step.
     import inspect
     kinds = {"swap_in": "swap_in", "store_swap_in": "swap_in", "store_swap_in_backup": "swap_in",
-             "swap_in_paged": "swap_in",
+             "swap_in_paged": "swap_in", "store_swap_in_paged_backup": "swap_in",
              "replay_plan": "replay", "backup": "backup"}
     per_step = {"swap_in": len(wl.anchors) * wl.spec, "replay": len(wl.skip_layers) * wl.spec,
                 "backup": wl.num_layers}
@@ -498,8 +498,8 @@ def main():
             "parallelism": "single GPU (requests are independent)",
             "prefetch": bool(g.prefetch) if wl.skip_layers else None,
             "layer_compute_mib": args.layer_compute_mib,
-            "fused_launches": ("store+swap-in+backup" if g.fuse_backup else "store+swap-in")
-                              if not wl.page_size else "none",
+            "fused_launches": "store+swap-in+backup" if g.fuse_backup else
+                              ("store+swap-in" if not wl.page_size else "none"),
         },
         "roofline": {
             "kernel": "swap_in_kernel",

@@ -1228,17 +1228,37 @@ int hisparse_store_swap_in_backup(hisparse_ctx* c, int32_t anchor_layer, const v
                           nullptr, 0, 0, 1, 0, new_rows, true, stream);
 }
 
+namespace {
+
+bool paged_args_ok(const hisparse_ctx* c, const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                   int32_t hot_row_base)
+{
+    if (!c || page_size < 1 || max_pages < 0 || (max_pages > 0 && !block_table) || hot_row_base < 0) return false;
+    return static_cast<long long>(hot_row_base) + static_cast<long long>(c->R) * (c->B + 1) <= INT_MAX;
+}
+
+}  // namespace
+
 int hisparse_swap_in_paged(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_idx, const int32_t* seq_lens,
                            const int32_t* block_table, int32_t max_pages, int32_t page_size, int32_t hot_row_base,
                            const int32_t* req_idx, int32_t nb, int32_t* out_rows, hisparse_plan plan_row,
                            hipStream_t stream)
 {
-    if (!c || page_size < 1 || max_pages < 0 || (max_pages > 0 && !block_table) || hot_row_base < 0)
-        return HISPARSE_EINVAL;
-    if (static_cast<long long>(hot_row_base) + static_cast<long long>(c->R) * (c->B + 1) > INT_MAX)
-        return HISPARSE_EINVAL;
+    if (!paged_args_ok(c, block_table, max_pages, page_size, hot_row_base)) return HISPARSE_EINVAL;
     return launch_swap_in(c, anchor_layer, topk_idx, seq_lens, nullptr, req_idx, nb, out_rows, plan_row,
                           block_table, 1, max_pages, page_size, hot_row_base, nullptr, false, stream);
+}
+
+int hisparse_store_swap_in_paged_backup(hisparse_ctx* c, int32_t anchor_layer, const void* new_rows,
+                                        const int32_t* topk_idx, const int32_t* seq_lens, const int32_t* block_table,
+                                        int32_t max_pages, int32_t page_size, int32_t hot_row_base,
+                                        const int32_t* req_idx, int32_t nb, int32_t* out_rows,
+                                        hisparse_plan plan_row, hipStream_t stream)
+{
+    if (!paged_args_ok(c, block_table, max_pages, page_size, hot_row_base)) return HISPARSE_EINVAL;
+    if (!new_rows || !aligned16(new_rows)) return HISPARSE_EINVAL;
+    return launch_swap_in(c, anchor_layer, topk_idx, seq_lens, nullptr, req_idx, nb, out_rows, plan_row,
+                          block_table, 1, max_pages, page_size, hot_row_base, new_rows, true, stream);
 }
 
 int hisparse_replay_plan(hisparse_ctx* c, int32_t skip_layer, hisparse_plan plan_row, const int32_t* req_idx,

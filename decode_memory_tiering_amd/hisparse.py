@@ -37,6 +37,7 @@ HISPARSE_HOST_NONCOHERENT = 2
 EXPORTS = (
     "hisparse_init", "hisparse_destroy", "hisparse_admit", "hisparse_store_newest",
     "hisparse_swap_in", "hisparse_store_swap_in", "hisparse_store_swap_in_backup", "hisparse_swap_in_paged",
+    "hisparse_store_swap_in_paged_backup",
     "hisparse_replay_plan", "hisparse_backup", "hisparse_spill", "hisparse_import", "hisparse_get_state",
     "hisparse_set_state", "hisparse_get_error", "hisparse_host_alloc", "hisparse_host_free",
     "hisparse_swap_in_lds_bytes", "hisparse_strerror", "hisparse_version",
@@ -95,6 +96,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hisparse_store_swap_in.argtypes = [P, I32, P, P, P, P, P, I32, P, hisparse_plan, P]
     lib.hisparse_store_swap_in_backup.argtypes = [P, I32, P, P, P, P, P, I32, P, hisparse_plan, P]
     lib.hisparse_swap_in_paged.argtypes = [P, I32, P, P, P, I32, I32, I32, P, I32, P, hisparse_plan, P]
+    lib.hisparse_store_swap_in_paged_backup.argtypes = [P, I32, P, P, P, P, I32, I32, I32, P, I32, P,
+                                                        hisparse_plan, P]
     lib.hisparse_replay_plan.argtypes = [P, I32, hisparse_plan, P, I32, P]
     lib.hisparse_backup.argtypes = [P, I32, P, P, P, I32, P]
     lib.hisparse_spill.argtypes = [P, I32, P, I32, I32, P, I32, P]
@@ -231,6 +234,17 @@ def hisparse_swap_in_paged(ctx: int, anchor_layer: int, topk_idx, seq_lens, bloc
                                          max_pages, page_size, hot_row_base, _ptr(req_idx),
                                          int(topk_idx.shape[0]), _ptr(out_rows), plan.c(), _stream(stream)),
            "hisparse_swap_in_paged")
+
+
+def hisparse_store_swap_in_paged_backup(ctx: int, anchor_layer: int, new_rows, topk_idx, seq_lens, block_table,
+                                        page_size: int, hot_row_base: int, req_idx, out_rows, plan: Plan,
+                                        stream=None) -> None:
+    max_pages = 0 if block_table is None else int(block_table.shape[1])
+    _check(_lib().hisparse_store_swap_in_paged_backup(ctx, anchor_layer, _ptr(new_rows), _ptr(topk_idx),
+                                                      _ptr(seq_lens), _ptr(block_table), max_pages, page_size,
+                                                      hot_row_base, _ptr(req_idx), int(topk_idx.shape[0]),
+                                                      _ptr(out_rows), plan.c(), _stream(stream)),
+           "hisparse_store_swap_in_paged_backup")
 
 
 def hisparse_replay_plan(ctx: int, skip_layer: int, plan: Plan, req_idx=None, stream=None) -> None:
@@ -389,6 +403,11 @@ class HiSparseCache:
                       plan, stream=None):
         hisparse_swap_in_paged(self.ctx, anchor, topk_idx, seq_lens, block_table, page_size, hot_row_base,
                                req_idx, out_rows, plan, stream)
+
+    def store_swap_in_paged_backup(self, anchor, new_rows, topk_idx, seq_lens, block_table, page_size,
+                                   hot_row_base, req_idx, out_rows, plan, stream=None):
+        hisparse_store_swap_in_paged_backup(self.ctx, anchor, new_rows, topk_idx, seq_lens, block_table, page_size,
+                                            hot_row_base, req_idx, out_rows, plan, stream)
 
     def replay_plan(self, skip_layer, plan, req_idx=None, stream=None):
         hisparse_replay_plan(self.ctx, skip_layer, plan, req_idx, stream)

@@ -150,14 +150,19 @@ class GpuRun:
         main = torch.cuda.current_stream(self.dev)
         for l in range(wl.num_layers):
             g = wl.anchor_of[l]
-            fused = self.fuse_store and g == l and not self.paged
+            # the paged path fuses the KV write only together with the backup
+            fused = self.fuse_store and g == l and (not self.paged or self.fuse_backup)
             if not fused:
                 c.store_newest(l, new_kv[l], seq_lens, self.resident)
             if self.paged and seq_lens_np is not None:
                 self.store_newest_resident(l, new_kv[l], seq_lens_np)
             if g == l:
                 for s in range(wl.spec):
-                    if self.paged:
+                    if self.paged and fused and s == 0:
+                        c.store_swap_in_paged_backup(l, new_kv[l], topk[l][s], seq_lens, self.block_table,
+                                                     wl.page_size, self.hot_row_base, None, self.out[l][s],
+                                                     plans[l][s])
+                    elif self.paged:
                         c.swap_in_paged(l, topk[l][s], seq_lens, self.block_table, wl.page_size,
                                         self.hot_row_base, None, self.out[l][s], plans[l][s])
                     elif fused and s == 0:

@@ -233,6 +233,21 @@ int hisparse_swap_in_paged(hisparse_ctx* ctx, int32_t anchor_layer,
                            int32_t hot_row_base, const int32_t* req_idx, int32_t nb,
                            int32_t* out_rows, hisparse_plan plan_row, hipStream_t stream);
 
+/* hisparse_store_newest, hisparse_swap_in_paged and hisparse_backup on the
+ * anchor layer in one launch, as hisparse_store_swap_in_backup is for
+ * hisparse_swap_in: each new row goes to the newest token's hot row (L-1
+ * when L <= B, else B) and to host[anchor][r][L-1] (not for L > max_seq_len,
+ * which sets HISPARSE_DERR_SEQ_LEN).  A resident copy of the newest token,
+ * when its page is resident, stays the caller's write to its resident cache,
+ * as with the separate calls.  Host checks as hisparse_swap_in_paged, and
+ * new_rows must be 16-byte aligned.  [SGL] "Decode Workflow"; [vLLM]
+ * "Resident device pages", "Performance invariants". */
+int hisparse_store_swap_in_paged_backup(hisparse_ctx* ctx, int32_t anchor_layer, const void* new_rows,
+                                        const int32_t* topk_idx, const int32_t* seq_lens,
+                                        const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                                        int32_t hot_row_base, const int32_t* req_idx, int32_t nb,
+                                        int32_t* out_rows, hisparse_plan plan_row, hipStream_t stream);
+
 /* Copy-only replay of an anchor's plan row on a skip layer: for each batch
  * row b and m < count[b], hot[skip][r][slot] <- host[skip][r][pos].  Runs on
  * a small fixed grid (replay_grid workgroups) so it can overlap other work on

@@ -585,3 +585,17 @@ def test_fused_backup_matches_separate_calls_and_skips_rows_past_the_pool():
     assert np.array_equal(o1, o2) and np.array_equal(hot1, hot2) and np.array_equal(host1, host2)
     assert e1 == e2 == H.HISPARSE_DERR_SEQ_LEN
     assert np.array_equal(host1[0, L[0] - 1], new[0]) and np.array_equal(host1[2, L[2] - 1], new[2])
+
+
+def test_paged_fused_backup_host_checks():
+    c = _cache()
+    t = torch.zeros(1, c.K, dtype=torch.int32, device="cuda")
+    L = torch.full((1,), 10, dtype=torch.int32, device="cuda")
+    rows = torch.zeros(c.rb + 16, dtype=torch.uint8, device="cuda")
+    for kw in (dict(page_size=0, hot_row_base=0, new=rows[:c.rb]), dict(page_size=4, hot_row_base=-1, new=rows[:c.rb]),
+               dict(page_size=4, hot_row_base=0, new=rows[8:8 + c.rb])):          # new rows not 16-byte aligned
+        with pytest.raises(H.HisparseError) as e:
+            c.store_swap_in_paged_backup(0, kw["new"], t, L, None, kw["page_size"], kw["hot_row_base"], None,
+                                         t.clone(), H.Plan.empty(1, c.K))
+        assert e.value.rc == H.HISPARSE_EINVAL
+    c.close()

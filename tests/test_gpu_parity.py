@@ -150,9 +150,11 @@ PAGED = [
 ]
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
 @pytest.mark.parametrize("wl", PAGED, ids=[w.name for w in PAGED])
-def test_paged_geometries(wl):
-    _lockstep(wl)
+def test_paged_geometries(wl, fused):
+    # fused: store + paged swap-in + backup in one launch; separate: three launches
+    _lockstep(wl, fuse_store=fused)
 
 
 @pytest.mark.timeout(600)
@@ -185,7 +187,7 @@ def test_random_geometries(seed):
     wl = _random_workload(seed)
     blocks = [b for b in (128, 256, 512, 768, 1024) if _launch_shape_fits(wl, b)]
     block = blocks[seed % len(blocks)]
-    _lockstep(wl, block_size=block, prefetch=bool(seed % 2))
+    _lockstep(wl, block_size=block, prefetch=bool(seed % 2), fuse_store=seed % 4 != 3)
 
 
 def test_buffer_above_8192_slots():
