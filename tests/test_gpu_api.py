@@ -599,3 +599,56 @@ def test_paged_fused_backup_host_checks():
                                          t.clone(), H.Plan.empty(1, c.K))
         assert e.value.rc == H.HISPARSE_EINVAL
     c.close()
+
+
+def test_anchor_layers_and_replays_on_concurrent_streams():
+    """Calls on different anchor layers, and replays of different skip
+    layers, may run concurrently: two anchors resolved on two streams at once,
+    each anchor's skip layer replayed on a third and fourth stream, must equal
+    the oracle's sequential steps."""
+    R, B, K, rb, max_seq = 8, 96, 32, 48, 700
+    layers, anchor_of = 4, (0, 0, 2, 2)
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq, layers=layers, anchor_of=anchor_of)
+    o = _oracle_for(c)
+    rng = np.random.default_rng(17)
+    L = rng.integers(60, 500, size=R).astype(np.int32)
+    for g in (0, 2):
+        c.admit(g, _dev(np.arange(R)), _dev(L - 1))
+        o.admit(g, np.arange(R), L - 1)
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    outs = {g: torch.empty(R, K, dtype=torch.int32, device="cuda") for g in (0, 2)}
+    plans = {g: H.Plan.empty(R, K) for g in (0, 2)}
+    torch.cuda.synchronize()
+    for step in range(6):
+        topk = {g: np.stack([rng.choice(int(x), size=K, replace=False) for x in L]).astype(np.int32) for g in (0, 2)}
+        new = rng.integers(0, 256, size=(layers, R, rb), dtype=np.uint8)
+        topk_d = {g: _dev(v) for g, v in topk.items()}
+        new_d = _dev(new, torch.uint8)
+        L_d = _dev(L)
+        torch.cuda.synchronize()
+        for i, (g, x) in enumerate(((0, 1), (2, 3))):
+            main, side = streams[i], streams[2 + i]
+            with torch.cuda.stream(main):
+                c.store_swap_in_backup(g, new_d[g], topk_d[g], L_d, None, None, outs[g], plans[g], stream=main)
+                c.store_newest(x, new_d[x], L_d, stream=main)
+                ev = torch.cuda.Event()
+                ev.record(main)
+            side.wait_event(ev)
+            c.replay_plan(x, plans[g], None, side)
+            c.backup(x, L_d, stream=side)
+        torch.cuda.synchronize()
+        for g, x in ((0, 1), (2, 3)):
+            o.store_newest(g, new[g], L)
+            eo, ep = o.swap_in(g, topk[g], L)
+            o.backup(g, L)
+            o.store_newest(x, new[x], L)
+            o.replay(x, ep)
+            o.backup(x, L)
+            assert np.array_equal(outs[g].cpu().numpy(), eo), f"step {step} anchor {g}"
+            assert np.array_equal(plans[g].count.cpu().numpy(), ep.count)
+        L = L + 1
+    for l in range(layers):
+        assert np.array_equal(c.hot[l].cpu().numpy(), o.hot[l]), f"hot {l}"
+        assert np.array_equal(c.host_np[l], o.host[l]), f"host {l}"
+    assert c.get_error() == 0
+    c.close()
