@@ -75,6 +75,7 @@ class GpuRun:
             self.hot_row_base = n_phys * wl.page_size
             self.res_cache = [torch.zeros(n_phys * wl.page_size, wl.rb, dtype=torch.uint8, device=self.dev)
                               for _ in range(wl.num_layers)]
+            self._resident_newest = {}
         if fill:
             self.fill_and_admit()
 
@@ -112,17 +113,24 @@ class GpuRun:
                 self.res_cache[l][ph * P: ph * P + (hi - lo)].copy_(host[r, lo:hi], non_blocking=False)
 
     def store_newest_resident(self, layer: int, new_kv_l, seq_lens_np):
-        """The forward's KV write for requests whose newest page is resident."""
-        P = self.wl.page_size
-        pg = (seq_lens_np - 1) // P
-        rows = []
-        for r in range(self.wl.R):
-            ph = self.block_table_np[r, pg[r]] if pg[r] < self.block_table_np.shape[1] else -1
-            if ph >= 0:
-                rows.append((r, ph * P + (seq_lens_np[r] - 1) % P))
-        if rows:
-            src = self.torch.tensor([int(r) for r, _ in rows], dtype=self.torch.long, device=self.dev)
-            dst = self.torch.tensor([int(d) for _, d in rows], dtype=self.torch.long, device=self.dev)
+        """The forward's KV write for requests whose newest page is resident.
+        The (request, resident row) pairs of a step depend only on the
+        sequence lengths, so they are computed once per distinct lengths and
+        kept on the device: a repeated decode costs no host work here."""
+        key = seq_lens_np.tobytes()
+        idx = self._resident_newest.get(key)
+        if idx is None:
+            P, bt = self.wl.page_size, self.block_table_np
+            pg = (seq_lens_np.astype(np.int64) - 1) // P
+            inside = pg < bt.shape[1]
+            phys = np.where(inside, bt[np.arange(self.wl.R), np.minimum(pg, bt.shape[1] - 1)], -1)
+            rows = np.nonzero(phys >= 0)[0]
+            dst = phys[rows].astype(np.int64) * P + (seq_lens_np[rows].astype(np.int64) - 1) % P
+            idx = (self.torch.from_numpy(rows.astype(np.int64)).to(self.dev),
+                   self.torch.from_numpy(dst).to(self.dev)) if rows.size else None
+            self._resident_newest[key] = idx
+        if idx is not None:
+            src, dst = idx
             self.res_cache[layer].index_copy_(0, dst, new_kv_l.index_select(0, src))
 
     def row_view(self, layer: int):
