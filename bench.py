@@ -11,7 +11,8 @@ before timing; host pools live in pinned host memory, as the method intends.
 Prints one JSON line.  `value` = top-k entries resolved per second over the
 timed steps (all layers and verify rows), wall clock between two
 synchronisations; the median of --runs repetitions of the whole decode, each
-after re-admitting every request, so each repeats the first exactly.  The
+after re-admitting every request, so each repeats the first exactly (one more
+repetition goes first and is discarded, to warm up).  The
 resolver's launch durations come from HIP events recorded in the timed runs,
 spread over them so that each step's launches are timed in exactly one run
 (a timed launch costs its step about 7 us of event overhead).  `roofline` describes the swap-in kernel: its miss copy is
@@ -394,15 +395,18 @@ def main():
 
     # every run re-admits all requests and repeats the same decode exactly:
     # W untimed warmup steps, then exactly K timed steps between two
-    # synchronisations
+    # synchronisations.  One whole run goes first, discarded, to warm the GPU
+    # and the host pool's first touches.
+    for k in range(total):
+        run(k)
+    torch.cuda.synchronize(dev)
     walls = []
     for name in kinds:
         setattr(g.cache, name, timed(name, origs[name]))
     try:
         for i in range(args.runs + 1):
             detail = i == args.runs
-            if i:
-                g.readmit()
+            g.readmit()
             recording.clear()
             for k in range(args.warmup):
                 run(k)

