@@ -40,8 +40,10 @@ def _dev(a, dtype=torch.int32):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype)
 
 
-def test_request_subsets_via_req_idx():
-    """Each step only some requests decode, in a shuffled batch order."""
+@pytest.mark.parametrize("form", ["separate", "fused"])
+def test_request_subsets_via_req_idx(form):
+    """Each step only some requests decode, in a shuffled batch order (three
+    launches, or the one fused launch)."""
     R, B, K, rb, max_seq = 10, 64, 24, 32, 600
     c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
     o = _oracle_for(c)
@@ -60,9 +62,12 @@ def test_request_subsets_via_req_idx():
         new = rng.integers(0, 256, size=(nb, rb), dtype=np.uint8)
         out = torch.empty(nb, K, dtype=torch.int32, device="cuda")
         plan = H.Plan.empty(nb, K)
-        c.store_newest(0, _dev(new, torch.uint8), _dev(Lb), None, _dev(idx))
-        c.swap_in(0, _dev(topk), _dev(Lb), None, _dev(idx), out, plan)
-        c.backup(0, _dev(Lb), None, _dev(idx))
+        if form == "fused":
+            c.store_swap_in_backup(0, _dev(new, torch.uint8), _dev(topk), _dev(Lb), None, _dev(idx), out, plan)
+        else:
+            c.store_newest(0, _dev(new, torch.uint8), _dev(Lb), None, _dev(idx))
+            c.swap_in(0, _dev(topk), _dev(Lb), None, _dev(idx), out, plan)
+            c.backup(0, _dev(Lb), None, _dev(idx))
         o.store_newest(0, new, Lb, None, idx)
         eo, ep = o.swap_in(0, topk, Lb, None, idx)
         o.backup(0, Lb, None, idx)
@@ -650,5 +655,49 @@ def test_anchor_layers_and_replays_on_concurrent_streams():
     for l in range(layers):
         assert np.array_equal(c.hot[l].cpu().numpy(), o.hot[l]), f"hot {l}"
         assert np.array_equal(c.host_np[l], o.host[l]), f"host {l}"
+    assert c.get_error() == 0
+    c.close()
+
+
+def test_paged_fused_request_subsets_via_req_idx():
+    """The fused paged launch with some requests per step in a shuffled batch
+    order: block-table rows follow the batch rows, state and buffers the
+    requests."""
+    R, B, K, rb, max_seq, P = 8, 64, 24, 32, 600, 16
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
+    o = _oracle_for(c)
+    rng = np.random.default_rng(21)
+    L = rng.integers(30, 300, size=R).astype(np.int32)
+    max_pages = (max_seq + P - 1) // P
+    n_phys = R * max_pages // 3
+    bt_full = -np.ones((R, max_pages), np.int32)
+    flat = rng.choice(R * max_pages, size=n_phys, replace=False)
+    bt_full.reshape(-1)[flat] = np.arange(n_phys, dtype=np.int32)
+    base = n_phys * P
+    req = np.arange(R, dtype=np.int32)
+    c.admit(0, _dev(req), _dev(L - 1))
+    o.admit(0, req, L - 1)
+    for step in range(10):
+        nb = int(rng.integers(1, R + 1))
+        idx = rng.permutation(R)[:nb].astype(np.int32)
+        Lb = L[idx]
+        topk = np.stack([rng.choice(int(x), size=K, replace=False) for x in Lb]).astype(np.int32)
+        new = rng.integers(0, 256, size=(nb, rb), dtype=np.uint8)
+        bt = np.ascontiguousarray(bt_full[idx])
+        out = torch.empty(nb, K, dtype=torch.int32, device="cuda")
+        plan = H.Plan.empty(nb, K)
+        c.store_swap_in_paged_backup(0, _dev(new, torch.uint8), _dev(topk), _dev(Lb), _dev(bt), P, base, _dev(idx),
+                                     out, plan)
+        o.store_newest(0, new, Lb, None, idx)
+        eo, ep = o.swap_in_paged(0, topk, Lb, bt, P, base, idx)
+        o.backup(0, Lb, None, idx)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eo), f"step {step}"
+        assert np.array_equal(plan.count.cpu().numpy(), ep.count)
+        lru, tok = c.get_state(0)
+        assert np.array_equal(lru.cpu().numpy(), o.lru[0]) and np.array_equal(tok.cpu().numpy(), o.tok[0])
+        L[idx] += 1
+    assert np.array_equal(c.hot[0].cpu().numpy(), o.hot[0])
+    assert np.array_equal(c.host_np[0], o.host[0])
     assert c.get_error() == 0
     c.close()
