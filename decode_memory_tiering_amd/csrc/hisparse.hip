@@ -5,14 +5,20 @@
 //                    hit detection, ballot-scan LRU compaction, victim
 //                    assignment, plan record and the miss copy from pinned
 //                    host memory, in one launch with one workgroup per
-//                    batch row.  SGLang guide "HiSparse: Hierarchical Sparse
-//                    Attention", "Decode Workflow"; vLLM design note "HiSparse
-//                    local KV offload architecture", "Resident device pages"
-//                    and "Hot lookup and LRU".
+//                    batch row; per-request or per-page residency; on
+//                    request, the forward's KV write and the eager backup
+//                    of the newest row in the same launch.  SGLang guide
+//                    "HiSparse: Hierarchical Sparse Attention", "Decode
+//                    Workflow"; vLLM design note "HiSparse local KV offload
+//                    architecture", "Resident device pages" and "Hot lookup
+//                    and LRU".
 //   replay_kernel    copy-only replay of a plan row on a skip layer, small
 //                    fixed grid.  SGLang guide, "Shared-index prefetch".
 //   backup_kernel    newest token's row, hot buffer -> host pool.  SGLang
 //                    guide, "Decode Workflow" (eager backup).
+//   page_copy_kernel whole pages: resident -> host (spill), staging -> host
+//                    with an optional resident mirror (import).  vLLM design
+//                    note, "Spill transaction" and "P/D import target".
 //   store_newest_kernel, admit_*_kernel, init_state_kernel: the forward's KV
 //                    write, request admission, context set-up.
 //
@@ -39,7 +45,7 @@ constexpr int kMaxK = 4096;
 constexpr int kDefaultBlock = 1024;
 constexpr int kDefaultReplayGrid = 12;   // enough to fill the host link without crowding the fabric (measured)
 // Copy-loop shape: batches of kCopyUnroll 16-byte loads per thread, kCopyBuffers
-// batches in rotation (measured on MI355X; see copy_rows).  The swap-in's
+// batches in rotation (measured on MI355X; see RowCopy).  The swap-in's
 // miss copy runs in every slow batch row's workgroup at once (up to one per
 // CU), so it keeps fewer loads in flight per thread than the replay's small
 // grid does: 4 x 2 measured best across the workloads (8 x 2 and 2 x 2 were
@@ -110,8 +116,8 @@ __device__ int wave_exclusive_scan(int* a, int n)
     return __shfl(incl, kWave - 1, kWave);
 }
 
-// Copy `rows` rows of rb bytes (rb % 16 == 0) from src rows to dst rows, the
-// row numbers given by src_row(m) / dst_row(m).  Chunk c of the flattened
+// RowCopy / copy_rows: copy `rows` rows of rb bytes (rb % 16 == 0) from src
+// rows to dst rows, the row numbers given by src_row(m) / dst_row(m).  Chunk c of the flattened
 // (row, 16-byte column) space goes to thread c % nthr; the (row, column) walk
 // is incremental, so no chunk needs a division.
 //
@@ -477,8 +483,9 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
 
     // -- hit detection: probe every slot's position ----------------------
     // A thread's probes advance in lockstep, one table entry per round, in
-    // groups of up to 8 chains, so their LDS reads overlap instead of running
-    // one chain after another.
+    // groups of up to 8 chains.  (Each chain's read still waits on its own
+    // result before the next chain's; the workgroup's 16 waves are what keep
+    // the LDS busy, so the phase is bound by LDS throughput, not latency.)
     constexpr int kG = EB < 8 ? EB : 8;
 #pragma unroll
     for (int g0 = 0; g0 < EB; g0 += kG) {
