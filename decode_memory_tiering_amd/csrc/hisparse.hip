@@ -1009,6 +1009,15 @@ bool is_device_memory(void* p, size_t bytes)
     return at.type == hipMemoryTypeDevice;
 }
 
+// A context is used on the device that was current at init: any other
+// current device would launch its kernels with another device's pointers.
+bool usable(const hisparse_ctx* c)
+{
+    int d = -1;
+    if (!c || hipGetDevice(&d) != hipSuccess) return false;
+    return d == c->device;
+}
+
 bool is_anchor(const hisparse_ctx* c, int32_t l)
 {
     return l >= 0 && l < c->layers && c->anchor_of[l] == l;
@@ -1152,7 +1161,7 @@ void hisparse_destroy(hisparse_ctx* c)
 int hisparse_admit(hisparse_ctx* c, int32_t anchor_layer, const int32_t* req_ids, const int32_t* seq_len0,
                    int32_t n, hipStream_t stream)
 {
-    if (!c || !is_anchor(c, anchor_layer) || n < 0 || n > c->R) return HISPARSE_EINVAL;
+    if (!usable(c) || !is_anchor(c, anchor_layer) || n < 0 || n > c->R) return HISPARSE_EINVAL;
     if (n == 0) return HISPARSE_OK;
     if (!req_ids || !seq_len0) return HISPARSE_EINVAL;
     hipLaunchKernelGGL(admit_state_kernel, dim3(n), dim3(256), 0, stream, c->lru[anchor_layer],
@@ -1168,7 +1177,7 @@ int hisparse_admit(hisparse_ctx* c, int32_t anchor_layer, const int32_t* req_ids
 int hisparse_store_newest(hisparse_ctx* c, int32_t layer, const void* new_rows, const int32_t* seq_lens,
                           const uint8_t* resident_mask, const int32_t* req_idx, int32_t nb, hipStream_t stream)
 {
-    if (!c || layer < 0 || layer >= c->layers || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
+    if (!usable(c) || layer < 0 || layer >= c->layers || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
     if (nb == 0) return HISPARSE_OK;
     if (!new_rows || !seq_lens || !aligned16(new_rows)) return HISPARSE_EINVAL;
     RowArgs a{};
@@ -1187,7 +1196,7 @@ int launch_swap_in(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_id
                    int32_t page_size, int32_t hot_row_base, const void* new_rows, bool backup,
                    hipStream_t stream)
 {
-    if (!c || !is_anchor(c, anchor_layer) || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
+    if (!usable(c) || !is_anchor(c, anchor_layer) || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
     if (nb == 0) return HISPARSE_OK;
     if (!topk_idx || !seq_lens || !out || !plan_row.pos || !plan_row.slot || !plan_row.count)
         return HISPARSE_EINVAL;
@@ -1240,7 +1249,8 @@ namespace {
 bool paged_args_ok(const hisparse_ctx* c, const int32_t* block_table, int32_t max_pages, int32_t page_size,
                    int32_t hot_row_base)
 {
-    if (!c || page_size < 1 || max_pages < 0 || (max_pages > 0 && !block_table) || hot_row_base < 0) return false;
+    if (!usable(c) || page_size < 1 || max_pages < 0 || (max_pages > 0 && !block_table) || hot_row_base < 0)
+        return false;
     return static_cast<long long>(hot_row_base) + static_cast<long long>(c->R) * (c->B + 1) <= INT_MAX;
 }
 
@@ -1271,7 +1281,7 @@ int hisparse_store_swap_in_paged_backup(hisparse_ctx* c, int32_t anchor_layer, c
 int hisparse_replay_plan(hisparse_ctx* c, int32_t skip_layer, hisparse_plan plan_row, const int32_t* req_idx,
                          int32_t nb, hipStream_t side_stream)
 {
-    if (!c || skip_layer < 0 || skip_layer >= c->layers || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
+    if (!usable(c) || skip_layer < 0 || skip_layer >= c->layers || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
     if (nb == 0) return HISPARSE_OK;
     if (!plan_row.pos || !plan_row.slot || !plan_row.count) return HISPARSE_EINVAL;
     ReplayArgs a{};
@@ -1289,7 +1299,7 @@ constexpr int kPageCopyGrid = 256;
 int launch_page_copy(hisparse_ctx* c, int32_t layer, const void* src, int32_t src_pages, int32_t page_size,
                      void* mirror, int32_t mirror_pages, const int32_t* transfers, int32_t n, hipStream_t stream)
 {
-    if (!c || layer < 0 || layer >= c->layers || n < 0 || page_size < 1 || src_pages < 0 || mirror_pages < 0)
+    if (!usable(c) || layer < 0 || layer >= c->layers || n < 0 || page_size < 1 || src_pages < 0 || mirror_pages < 0)
         return HISPARSE_EINVAL;
     if (n == 0) return HISPARSE_OK;
     if (!src || !transfers || !aligned16(src) || (mirror_pages > 0 && (!mirror || !aligned16(mirror))))
@@ -1322,7 +1332,7 @@ int hisparse_import(hisparse_ctx* c, int32_t layer, const void* staging, int32_t
 int hisparse_backup(hisparse_ctx* c, int32_t layer, const int32_t* seq_lens, const uint8_t* resident_mask,
                     const int32_t* req_idx, int32_t nb, hipStream_t stream)
 {
-    if (!c || layer < 0 || layer >= c->layers || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
+    if (!usable(c) || layer < 0 || layer >= c->layers || nb < 0 || nb > c->R) return HISPARSE_EINVAL;
     if (nb == 0) return HISPARSE_OK;
     if (!seq_lens) return HISPARSE_EINVAL;
     RowArgs a{};
@@ -1335,7 +1345,7 @@ int hisparse_backup(hisparse_ctx* c, int32_t layer, const int32_t* seq_lens, con
 
 int hisparse_get_state(hisparse_ctx* c, int32_t anchor_layer, int32_t* lru, int32_t* slot_tok, hipStream_t stream)
 {
-    if (!c || !is_anchor(c, anchor_layer) || !lru || !slot_tok) return HISPARSE_EINVAL;
+    if (!usable(c) || !is_anchor(c, anchor_layer) || !lru || !slot_tok) return HISPARSE_EINVAL;
     const size_t bytes = size_t(c->R) * c->B * sizeof(int32_t);
     hipError_t e = hipMemcpyAsync(lru, c->lru[anchor_layer], bytes, hipMemcpyDeviceToDevice, stream);
     if (e == hipSuccess) e = hipMemcpyAsync(slot_tok, c->tok[anchor_layer], bytes, hipMemcpyDeviceToDevice, stream);
@@ -1345,7 +1355,7 @@ int hisparse_get_state(hisparse_ctx* c, int32_t anchor_layer, int32_t* lru, int3
 int hisparse_set_state(hisparse_ctx* c, int32_t anchor_layer, const int32_t* lru, const int32_t* slot_tok,
                        hipStream_t stream)
 {
-    if (!c || !is_anchor(c, anchor_layer) || !lru || !slot_tok) return HISPARSE_EINVAL;
+    if (!usable(c) || !is_anchor(c, anchor_layer) || !lru || !slot_tok) return HISPARSE_EINVAL;
     const size_t bytes = size_t(c->R) * c->B * sizeof(int32_t);
     hipError_t e = hipMemcpyAsync(c->lru[anchor_layer], lru, bytes, hipMemcpyDeviceToDevice, stream);
     if (e == hipSuccess) e = hipMemcpyAsync(c->tok[anchor_layer], slot_tok, bytes, hipMemcpyDeviceToDevice, stream);
@@ -1354,7 +1364,7 @@ int hisparse_set_state(hisparse_ctx* c, int32_t anchor_layer, const int32_t* lru
 
 int hisparse_get_error(hisparse_ctx* c, uint32_t* flags, int clear, hipStream_t stream)
 {
-    if (!c || !flags) return HISPARSE_EINVAL;
+    if (!usable(c) || !flags) return HISPARSE_EINVAL;
     hipError_t e = hipMemcpyAsync(flags, c->err, sizeof(uint32_t), hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess && clear) e = hipMemsetAsync(c->err, 0, sizeof(uint32_t), stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);

@@ -49,7 +49,9 @@
  * so must a call that writes a layer's host pool (backup,
  * store_swap_in_backup, spill, import) and a later one that may read the
  * rows it wrote; calls on different anchor layers, and replays of different
- * skip layers, may run concurrently.
+ * skip layers, may run concurrently.  A context belongs to the device that
+ * was current at hisparse_init: every later call on it must be made with that
+ * device current (else HISPARSE_EINVAL; the library never switches devices).
  *
  * Errors: a call returns 0, or a negative code: HISPARSE_EINVAL (bad argument
  * seen on the host), HISPARSE_ENOMEM, or HISPARSE_EHIP(e) = -(1000 + e) for a
