@@ -182,7 +182,7 @@ def _random_workload(seed):
                       seq_first=("uniform", 1, 3 * B + 10), seed=2000 + seed, **kw)
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_geometries(seed):
     wl = _random_workload(seed)
     blocks = [b for b in (128, 256, 512, 768, 1024) if _launch_shape_fits(wl, b)]
