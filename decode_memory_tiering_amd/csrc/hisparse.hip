@@ -531,27 +531,13 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
     }
     __syncthreads();
 
-    // -- ballots: hits along the LRU list, misses along the top-k row ----
-    int lp_b[EB];
-    uint32_t hbits = 0;
-#pragma unroll
-    for (int k = 0; k < EB; ++k) {
-        const int c = k * nwaves + wave, j = c * kWave + lane;
-        lp_b[k] = 0;
-        if (c < ncb) {
-            bool f = false;
-            if (j < B) {
-                int x = kEarlyLru ? lru_own[k] : lru[j];
-                if (x < 0 || x >= B) { err |= HISPARSE_DERR_STATE; x = 0; }
-                lru_own[k] = x;
-                f = s.hit[x] != 0;
-            }
-            const uint64_t m = __ballot(f);
-            lp_b[k] = lanes_below(m);
-            hbits |= uint32_t(f) << k;
-            if (lane == 0) s.cnt_b[c] = __popcll(m);
-        }
-    }
+    // -- misses along the top-k row, their ranks, the first copy loads -----
+    // The m-th miss reads host row plan_t[m]; that is known as soon as the
+    // miss ranks are, so the first batch of the copy's loads is issued
+    // before the hits along the LRU list are even counted, and is in flight
+    // while the LRU list is reordered and the victims are chosen (the copy's
+    // stores wait for those).  Nothing global is written before the checks
+    // below, so a row that fails them still changes nothing.
     int lp_k[EK];
     uint32_t mbits = 0;
 #pragma unroll
@@ -566,34 +552,13 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
             if (lane == 0) s.cnt_k[c] = __popcll(m);
         }
     }
-    if (__syncthreads_or(err != 0)) {
-        fail_row(a, b, err);
-        return;
-    }
-
-    // -- chunk prefix sums -------------------------------------------------
+    __syncthreads();
     if (wave == 0) {
-        const int n_hit = wave_exclusive_scan(s.cnt_b, ncb);
-        if (lane == 0) s.totals[0] = n_hit;
-    }
-    if (wave == (nwaves > 1 ? 1 : 0)) {
         const int n_miss = wave_exclusive_scan(s.cnt_k, nck);
         if (lane == 0) s.totals[1] = n_miss;
     }
     __syncthreads();
-
-    const int n_hit = s.totals[0], M = s.totals[1];
-    const int n_keep = B - n_hit;   // non-hit slots; >= M because K <= B
-    if (n_keep < M) {               // only when the LRU list repeats a slot
-        fail_row(a, b, HISPARSE_DERR_STATE);
-        return;
-    }
-
-    // -- miss positions, then the first copy loads ---------------------------
-    // The m-th miss reads host row plan_t[m]; that is known as soon as the
-    // miss ranks are, so the first batch of the copy's loads is issued here
-    // and is in flight while the LRU list is reordered and the victims are
-    // chosen (the copy's stores wait for those).
+    const int M = s.totals[1];
     int m_own[EK];
 #pragma unroll
     for (int k = 0; k < EK; ++k) {
@@ -614,6 +579,43 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
                                                                [pt](int m) { return pt[m]; },
                                                                [pv](int m) { return pv[m]; });
     copy.prime();
+
+    // -- hits along the LRU list and their ranks ---------------------------
+    int lp_b[EB];
+    uint32_t hbits = 0;
+#pragma unroll
+    for (int k = 0; k < EB; ++k) {
+        const int c = k * nwaves + wave, j = c * kWave + lane;
+        lp_b[k] = 0;
+        if (c < ncb) {
+            bool f = false;
+            if (j < B) {
+                int x = kEarlyLru ? lru_own[k] : lru[j];
+                if (x < 0 || x >= B) { err |= HISPARSE_DERR_STATE; x = 0; }
+                lru_own[k] = x;
+                f = s.hit[x] != 0;
+            }
+            const uint64_t m = __ballot(f);
+            lp_b[k] = lanes_below(m);
+            hbits |= uint32_t(f) << k;
+            if (lane == 0) s.cnt_b[c] = __popcll(m);
+        }
+    }
+    if (__syncthreads_or(err != 0)) {
+        fail_row(a, b, err);
+        return;
+    }
+    if (wave == 0) {
+        const int n_hit = wave_exclusive_scan(s.cnt_b, ncb);
+        if (lane == 0) s.totals[0] = n_hit;
+    }
+    __syncthreads();
+    const int n_hit = s.totals[0];
+    const int n_keep = B - n_hit;   // non-hit slots; >= M because K <= B
+    if (n_keep < M) {               // only when the LRU list repeats a slot
+        fail_row(a, b, HISPARSE_DERR_STATE);
+        return;
+    }
 
     // -- LRU reorder and victim choice ------------------------------------
     // new order: non-hit slots n >= M, then hit slots, then victims n < M.
