@@ -8,11 +8,16 @@ copy from pinned host memory), the skip layers' plan replay, and the eager
 backup.  Inputs (top-k rows, new KV rows) are generated and placed in HBM
 before timing; host pools live in pinned host memory, as the method intends.
 
+The default workload is the DSV3.2-shaped decode: 4 layers with their own
+host pools, 128 requests (32 fully resident), 40000-token sequences, top_k
+2048, a 6144-slot buffer, 1152-byte bf16 rows, eager backup every step.
 Prints one JSON line.  `value` = top-k entries resolved per second over the
 timed steps (all layers and verify rows), wall clock between two
 synchronisations; the median of --runs repetitions of the whole decode, each
 after re-admitting every request, so each repeats the first exactly (one more
-repetition goes first and is discarded, to warm up).  The
+repetition goes first and is discarded, to warm up).  `all_steps` gives the
+same rate over every step of the workload's whole decode from admission (the
+first steps find an empty buffer: all misses), and per-step times.  The
 resolver's launch durations come from HIP events recorded in the timed runs,
 spread over them so that each step's launches are timed in exactly one run
 (a timed launch costs its step about 7 us of event overhead).  `roofline` describes the swap-in kernel: its miss copy is
@@ -109,23 +114,42 @@ def measure_zero_copy(dev, R=128, rows=4096, rb=1152, grids=(256, 512, 1024)):
     return best
 
 
-def counter_bytes(workload):
-    """(fetched, written) bytes per swap-in launch from the committed
-    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain
-    copy), or None when there is none for this workload or the kernel source
-    changed since the counters were taken.  Fetched bytes are the host-link
-    reads of the miss rows plus the HBM metadata reads."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"swap_in_kernel_{workload}_counters.md")
-    src = os.path.join(ROOT, "decode_memory_tiering_amd", "csrc", "hisparse.hip")
-    if not os.path.exists(path):
-        return None
+def profile_fields(name):
+    """key: value lines of a committed profiles/ summary, or {} if absent."""
+    path = os.path.join(ROOT, "profiles", name)
     kv = {}
-    for line in open(path):
-        if ":" in line and not line.startswith(("#", "rocprofv3", "`")):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("src_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if os.path.exists(path):
+        for line in open(path):
+            if ":" in line and not line.startswith(("#", "rocprofv3", "`", "|", " ")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    return kv
+
+
+def _src_sha256():
+    import hashlib
+    src = os.path.join(ROOT, "decode_memory_tiering_amd", "csrc", "hisparse.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+
+
+def window_matches(kv, workload, steps, warmup, runs):
+    """A committed summary applies only to the exact decode window it was
+    taken on (workload, timed steps, warm-up steps, timed runs) and to the
+    kernel source it was taken with."""
+    want = dict(workload=workload, steps=str(steps), warmup=str(warmup), runs=str(runs), src_sha256=_src_sha256())
+    return bool(kv) and all(kv.get(k) == v for k, v in want.items())
+
+
+def counter_bytes(workload, steps, warmup, runs):
+    """(fetched, written) bytes per swap-in launch of the timed window, from
+    the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each
+    scaled by what it reads for a plain copy of known size); None unless the
+    summary was taken on exactly this window and this kernel source.  Fetched
+    bytes include the miss rows read over the host link and the HBM metadata
+    reads; written bytes the hot rows and metadata written to HBM and the
+    fused backup's rows written to the host pool."""
+    kv = profile_fields(f"swap_in_kernel_{workload}_counters.md")
+    if not window_matches(kv, workload, steps, warmup, runs):
         return None
     try:
         return float(kv["fetch_bytes_per_launch"]), float(kv["write_bytes_per_launch"])
@@ -133,10 +157,17 @@ def counter_bytes(workload):
         return None
 
 
-def counter_traffic(workload):
-    """Fetched + written bytes per swap-in launch (see counter_bytes), or None."""
-    fw = counter_bytes(workload)
-    return None if fw is None else fw[0] + fw[1]
+def trace_mean_us(workload, steps, warmup, runs):
+    """Mean duration of the timed window's swap-in launches in the committed
+    rocprofv3 kernel trace, or None unless it was taken on exactly this
+    window and kernel source."""
+    kv = profile_fields(f"swap_in_kernel_{workload}_kernel_trace.md")
+    if not window_matches(kv, workload, steps, warmup, runs):
+        return None
+    try:
+        return float(kv["swap_in_timed_mean_us"])
+    except (KeyError, ValueError):
+        return None
 
 
 def tier_shares(wl, topk_all, steps, misses, block_table=None):
@@ -176,60 +207,57 @@ def tier_shares(wl, topk_all, steps, misses, block_table=None):
                 hot_hit_rate=(n["hit"] / lookup) if lookup else None)
 
 
-def cpu_baseline(wl, steps, warmup, host_pools, topk_all, newkv_all, budget_s=10.0, max_threads=16):
+def cpu_baseline(wl, steps, warmup, host_pools, topk_all, newkv_all, budget_s=10.0, max_threads=16,
+                 pool_steps=None):
     """The oracle, as it stands, on the same inputs and the same timed steps
-    as the GPU (steps [warmup, steps) of the decode, the warmup steps run
-    untimed): the decode, re-admitted between repetitions, is repeated until
-    about budget_s of oracle time on one thread; then the same again with the
-    requests split over the host's cores, one share per thread (requests are
-    independent and the oracle keeps no global state, so the shares run side
-    by side).  The oracle's hot buffers are written once beforehand, so no
-    timed step pays for first-touch page faults."""
-    from concurrent.futures import ThreadPoolExecutor
+    as the GPU (steps [warmup, steps) of the decode, the warm-up steps run
+    untimed), driven from C (oracle/oracle_timing.c: no Python inside the
+    timed loop): the decode, re-admitted before every repetition, is
+    repeated until about budget_s of timed oracle work on one thread; then
+    the same with the requests split into one share per host core, a POSIX
+    thread each (requests are independent and the oracle keeps no global
+    state, so the shares run side by side, each through every step).  The
+    oracle's hot buffers are written once beforehand, so no timed step pays
+    for first-touch page faults."""
     from oracle.runner import OracleRun
-    o = OracleRun(wl, steps, host_pools=host_pools)
+    from oracle.timing import DecodeTimer
+    # host pools hold pool_steps steps' rows (the GPU run's sizing)
+    o = OracleRun(wl, pool_steps or steps, host_pools=host_pools)
     for h in o.orc.hot:
         h.fill(0)
-    per_step = [sum(int(np.count_nonzero(v >= 0)) for v in topk_all[k].values()) for k in range(steps)]
+    assert all(h.shape == p.shape for h, p in zip(o.orc.host, host_pools)), "host pools sized for another run"
+    timer = DecodeTimer(o, topk_all[:steps], newkv_all[:steps], first_timed=warmup)
+    per_rep = sum(int(np.count_nonzero(v >= 0)) for k in range(warmup, steps) for v in topk_all[k].values())
 
-    def sweep(call):
-        t_run, entries, done, reps = 0.0, 0, 0, 0
-        while t_run <= budget_s and reps < 1000:
-            o.readmit()
+    def sweep(threads):
+        t_run, reps = 0.0, 0
+        while t_run <= budget_s and reps < 10000:
+            t_run += timer.run(threads)
             reps += 1
-            for k in range(warmup):
-                call(k)
-            for k in range(warmup, steps):
-                t0 = time.perf_counter()
-                call(k)
-                t_run += time.perf_counter() - t0
-                entries += per_step[k]
-                done += 1
-                if t_run > budget_s:
-                    break
-        return t_run, entries, done, reps
+        return t_run, reps
 
-    t1, e1, done, reps = sweep(lambda k: o.step(k, topk_all[k], newkv_all[k]))
+    t1, reps1 = sweep(1)
     threads = max(1, min(len(os.sched_getaffinity(0)), max_threads, wl.R))
-    shares = [c for c in np.array_split(np.arange(wl.R, dtype=np.int32), threads) if c.size]
-    with ThreadPoolExecutor(len(shares)) as pool:
-        def parallel(k):
-            list(pool.map(lambda req: o.step(k, topk_all[k], newkv_all[k], req), shares))
-        tn, en, done_n, _ = sweep(parallel) if threads > 1 else (t1, e1, done, reps)
-    what = (f"{done} timed decode steps (steps {warmup}..{steps - 1} of the same decode as the GPU run, "
-            f"{reps} repetition(s), re-admitted in between, warmup steps untimed), all {wl.R} requests "
-            f"and {wl.num_layers} layer(s)")
-    return dict(value=e1 / t1, unit="top-k entries resolved/s", cores=1, kind="oracle",
-                sample=f"{what}, single thread, oracle time {t1:.2f}s",
-                threads=dict(value=en / tn, cores=len(shares),
-                             sample=f"{done_n} timed decode steps, requests split over {len(shares)} "
-                                    f"threads, oracle wall time {tn:.2f}s"))
+    tn, repsn = sweep(threads) if threads > 1 else (t1, reps1)
+    what = (f"steps {warmup}..{steps - 1} of the same decode as the GPU run (warm-up steps untimed), all "
+            f"{wl.R} requests and {wl.num_layers} layer(s), re-admitted before each repetition")
+    return dict(value=per_rep * reps1 / t1, unit="top-k entries resolved/s", cores=1, kind="oracle",
+                sample=f"{reps1} repetition(s) of {what}; single thread, timed oracle work {t1:.2f}s",
+                threads=dict(value=per_rep * repsn / tn, cores=threads,
+                             sample=f"{repsn} repetition(s), requests split into {threads} shares on "
+                                    f"{threads} threads, timed wall {tn:.2f}s"))
 
 
 def measure_page_copy(dev, W, args):
     """Spill (resident page -> host page) and host import (staging page ->
     host page, half mirrored to resident pages) on the paged decode's shape:
-    64-token pages of 1152-byte rows, 4096 pages per call."""
+    64-token pages of 1152-byte rows, 4096 pages per call, by the copy kernel
+    and by the copy engines (one DMA copy per run of pages contiguous on both
+    sides).  Two transfer lists: pages scattered over the pool (every page its
+    own copy) and whole runs of 64 consecutive pages (64 copies per call).
+    Then each spill form beside a 2 GiB device-to-device copy on another
+    stream (a stand-in for a layer's other work): how much the spill slows
+    that work, and the spill's own rate meanwhile."""
     import torch
     from decode_memory_tiering_amd.runner import GpuRun
     wl = W.WORKLOADS["paged_decode"]
@@ -238,50 +266,215 @@ def measure_page_copy(dev, W, args):
     rng = np.random.default_rng(0)
     max_pages = g.block_table_np.shape[1]
     n_res = g.res_cache[0].shape[0] // P
+    assert n_res >= n
     pick = rng.choice(wl.R * max_pages, size=n, replace=False)
     spill = np.stack([rng.choice(n_res, n, replace=False), pick // max_pages, pick % max_pages,
                       -np.ones(n, np.int64)], 1).astype(np.int32)
     stg = torch.randint(0, 255, (n * P, rb), dtype=torch.uint8, device=dev)
     mirror = np.where(np.arange(n) % 2 == 0, rng.choice(n_res, n, replace=False), -1)
     imp = np.stack([np.arange(n), pick // max_pages, pick % max_pages, mirror], 1).astype(np.int32)
-    spill_d, imp_d = torch.from_numpy(spill).to(dev), torch.from_numpy(imp).to(dev)
-    out = {}
-    for name, fn, nbytes in (("spill", lambda: g.cache.spill(0, g.res_cache[0], P, spill_d), n * P * rb),
-                             ("import", lambda: g.cache.import_pages(0, stg, P, g.res_cache[0], imp_d), n * P * rb)):
+    # runs: request q's host pages 0..63 from resident pages 64q..64q+63 (import: staging
+    # likewise, no mirror), so every run of 64 transfers is contiguous on both sides
+    q = np.arange(n)
+    spill_runs = np.stack([q, q // 64, q % 64, -np.ones(n, np.int64)], 1).astype(np.int32)
+    imp_runs = spill_runs.copy()
+    lists = {"scattered": (spill, imp), "runs64": (spill_runs, imp_runs)}
+    res0 = g.res_cache[0]
+
+    def timeit(fn, reps):
         fn()
         torch.cuda.synchronize(dev)
         times = []
-        for _ in range(max(args.steps, 3)):
+        for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()
             e1.record()
             torch.cuda.synchronize(dev)
             times.append(e0.elapsed_time(e1) * 1e-3)
-        t = float(np.mean(times))
-        out[name] = dict(pages=n, bytes_to_host=nbytes, mean_us=t * 1e6, gbps=nbytes / t / 1e9)
+        return float(np.mean(times))
+
+    out = {}
+    reps = max(args.steps, 3)
+    nbytes = n * P * rb
+    for lname, (sp, im) in lists.items():
+        sp_d, im_d = torch.from_numpy(sp).to(dev), torch.from_numpy(im).to(dev)
+        forms = {
+            "spill_kernel": lambda: g.cache.spill(0, res0, P, sp_d),
+            "spill_dma": lambda: g.cache.spill_dma(0, res0, P, sp),
+            "import_kernel": lambda: g.cache.import_pages(0, stg, P, res0, im_d),
+            "import_dma": lambda: g.cache.import_pages_dma(0, stg, P, res0, im),
+        }
+        for fname, fn in forms.items():
+            t0 = time.perf_counter()
+            fn()
+            host_us = (time.perf_counter() - t0) * 1e6          # the call's own (enqueue) time
+            torch.cuda.synchronize(dev)
+            t = timeit(fn, reps)
+            out[f"{lname}/{fname}"] = dict(pages=n, bytes_to_host=nbytes, mean_us=t * 1e6,
+                                           gbps=nbytes / t / 1e9, enqueue_us=host_us)
+            log(f"[bench] {lname}/{fname}: {nbytes / t / 1e9:.1f} GB/s, enqueue {host_us:.0f} us")
+    # beside a 2 GiB device copy on the main stream
+    m = 2048 << 20
+    csrc = torch.ones(m, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    side = torch.cuda.Stream(device=dev)
+    t_alone = timeit(lambda: cdst.copy_(csrc), reps)
+    overlap = {"compute_alone_us": t_alone * 1e6}
+    sp, _ = lists["scattered"]
+    sp_d = torch.from_numpy(sp).to(dev)
+    for fname, fn in (("spill_kernel", lambda s: g.cache.spill(0, res0, P, sp_d, s)),
+                      ("spill_dma", lambda s: g.cache.spill_dma(0, res0, P, sp, s))):
+        c_ms, s_ms = [], []
+        for _ in range(reps):
+            torch.cuda.synchronize(dev)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            main = torch.cuda.current_stream(dev)
+            e[0].record(main)
+            side.wait_event(e[0])
+            e[2].record(side)
+            fn(side)
+            e[3].record(side)
+            cdst.copy_(csrc)
+            e[1].record(main)
+            torch.cuda.synchronize(dev)
+            c_ms.append(e[0].elapsed_time(e[1]))
+            s_ms.append(e[2].elapsed_time(e[3]))
+        tc, ts = float(np.mean(c_ms)) * 1e-3, float(np.mean(s_ms)) * 1e-3
+        overlap[fname] = dict(compute_us=tc * 1e6, compute_slowdown=tc / t_alone, spill_us=ts * 1e6,
+                              spill_gbps=nbytes / ts / 1e9)
+        log(f"[bench] beside 2 GiB copy, {fname}: compute x{tc / t_alone:.3f}, spill {nbytes / ts / 1e9:.1f} GB/s")
     err = g.cache.get_error()
     g.close()
     if err:
         log(f"[bench] device error word {err:#x}")
         sys.exit(1)
     d2h = None if args.no_link else measure_link(dev, to_host=True)
-    print(json.dumps({"metric": "page transfer GB/s (device -> pinned host)", "value": out["spill"]["gbps"],
+    print(json.dumps({"metric": "page transfer GB/s (device -> pinned host)",
+                      "value": out["scattered/spill_kernel"]["gbps"],
                       "measured_d2h_link_gbps": d2h,
-                      "unit": "GB/s", "higher_is_better": True, "n_gpus": 1, "steps": max(args.steps, 3),
-                      "config": {"workload": "paged_decode pages", "page_size": P, "row_bytes": rb},
-                      "spill": out["spill"], "import": out["import"],
+                      "unit": "GB/s", "higher_is_better": True, "n_gpus": 1, "steps": reps,
+                      "config": {"workload": "paged_decode pages", "page_size": P, "row_bytes": rb, "pages": n},
+                      "forms": out, "beside_2gib_copy": overlap,
                       "peak": PCIE5_X16_GBPS}), flush=True)
+
+
+def algorithmic_bytes(wl, topk_all, steps, misses, fused_rows):
+    """Bytes the swap-in launches of the given steps must move, by where they
+    go: host-link reads (miss rows), host-link writes (rows the fused eager
+    backup writes), HBM reads (top-k rows, slot maps and LRU lists of slow
+    rows, new KV rows of a fused store) and HBM writes (miss rows landing in
+    the hot buffer, slot ids, LRU lists, slot-map updates, plan pairs and
+    counts, fused new rows)."""
+    from decode_memory_tiering_amd import workload as W
+    res = W.resident_mask(wl)
+    entries = slow = 0
+    for k in steps:
+        for v in topk_all[k].values():
+            entries += int(np.count_nonzero(v >= 0))
+        L = W.seq_lens_at(wl, k)
+        slow += int(np.count_nonzero((L > wl.B) & (res == 0))) * len(wl.anchors) * wl.spec
+    rb, B = wl.rb, wl.B
+    return dict(
+        host_link_read=misses * rb,
+        host_link_write=fused_rows * rb,
+        hbm_read=entries * 4 + slow * 8 * B + fused_rows * rb,
+        hbm_write=misses * rb + entries * 4 + slow * (4 * B + 4) + misses * 12 + fused_rows * rb,
+        entries=entries, slow_rows=slow)
+
+
+def measure_indexshare_overlap(dev, W, args):
+    """The IndexShare decode (one anchor + 3 skip layers replaying its miss
+    plan) with a 2 GiB device copy after every layer standing in for that
+    layer's other compute: the step time with the skip layers' replays
+    pre-issued on the side stream against the same decode with every replay
+    inline on the main stream, alternating, plus each replay launch's rate."""
+    import torch
+    from decode_memory_tiering_amd.hisparse import Plan
+    from decode_memory_tiering_amd.runner import GpuRun, draw_topk, new_kv_all_layers
+    wl = W.WORKLOADS["indexshare"]
+    total = args.warmup + args.steps
+    g = GpuRun(wl, total, prefetch=True)
+    streams = {a: W.TopkStream(wl, a) for a in wl.anchors}
+    topk_all = [draw_topk(wl, streams, k) for k in range(total)]
+    topk_dev = [{a: torch.from_numpy(v).to(dev) for a, v in t.items()} for t in topk_all]
+    newkv_dev = [new_kv_all_layers(wl, k, dev) for k in range(total)]
+    seq_dev = [g.seq_lens(k) for k in range(total)]
+    shared = {a: [Plan.empty(wl.R, wl.K, dev) for _ in range(wl.spec)] for a in wl.anchors}
+    step_plans = [{a: [Plan(p.pos, p.slot, torch.zeros(wl.R, dtype=torch.int32, device=dev))
+                       for p in shared[a]] for a in wl.anchors} for _ in range(total)]
+    n = (args.layer_compute_mib or 2048) << 20
+    csrc = torch.ones(n, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+
+    def decode(prefetch, replay_events=None):
+        g.prefetch = prefetch
+        g.readmit()
+        for k in range(args.warmup):
+            g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=lambda l: cdst.copy_(csrc))
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for k in range(args.warmup, total):
+            g.step(topk_dev[k], newkv_dev[k], seq_dev[k], plans=step_plans[k], between_layers=lambda l: cdst.copy_(csrc))
+        torch.cuda.synchronize(dev)
+        return (time.perf_counter() - t0) / args.steps
+
+    decode(True)
+    times = {True: [], False: []}
+    for _ in range(args.runs):
+        for pf in (True, False):
+            times[pf].append(decode(pf))
+    # one more prefetched decode with an event pair around every replay launch
+    orig = g.cache.replay_plan
+    ev = []
+
+    def timed_replay(skip, plan, req_idx=None, stream=None):
+        s = stream or torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        orig(skip, plan, req_idx, s)
+        e1.record(s)
+        ev.append((e0, e1))
+    g.cache.replay_plan = timed_replay
+    try:
+        decode(True)
+    finally:
+        g.cache.replay_plan = orig
+    rows = sum(int(p.count.sum().item()) for k in range(args.warmup, total) for x in wl.skip_layers
+               for p in step_plans[k][wl.anchor_of[x]])
+    ms = [a.elapsed_time(b) for a, b in ev[len(wl.skip_layers) * wl.spec * args.warmup:]]
+    err = g.cache.get_error()
+    g.close()
+    if err:
+        log(f"[bench] device error word {err:#x}")
+        sys.exit(1)
+    t_pf, t_in = float(np.median(times[True])), float(np.median(times[False]))
+    replay_t = float(np.mean(ms)) * 1e-3
+    print(json.dumps({
+        "metric": "IndexShare decode step time, skip-layer replays prefetched on a side stream vs inline",
+        "value": t_pf * 1e3, "unit": "ms/step", "higher_is_better": False, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "runs": args.runs,
+        "config": {"workload": wl.name, "requests": wl.R, "layers": wl.num_layers, "top_k": wl.K,
+                   "device_buffer_size": wl.B, "row_bytes": wl.rb, "layer_compute_mib": n >> 20},
+        "prefetch_ms_per_step": t_pf * 1e3, "inline_ms_per_step": t_in * 1e3,
+        "overlap_saving": 1.0 - t_pf / t_in,
+        "runs_ms": {"prefetch": [t * 1e3 for t in times[True]], "inline": [t * 1e3 for t in times[False]]},
+        "replay": {"launches": len(ms), "mean_launch_us": replay_t * 1e6, "rows_per_launch": rows / len(ms),
+                   "gbps": rows * wl.rb / len(ms) / replay_t / 1e9, "grid": "default (12 workgroups)"},
+    }), flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--runs", type=int, default=5,
                     help="repetitions of the whole timed decode (re-admitted in between); the median is reported")
-    ap.add_argument("--workload", default="fastpath_mix")
+    ap.add_argument("--workload", default="dsv32_decode")
+    ap.add_argument("--all-steps-runs", type=int, default=3,
+                    help="repetitions of the workload's whole decode from admission for the all_steps figure "
+                         "(0: skip it)")
     ap.add_argument("--block-size", type=int, default=0)
     ap.add_argument("--replay-grid", type=int, default=0)
     ap.add_argument("--host-flags", type=int, default=0)
@@ -292,8 +485,9 @@ def main():
     ap.add_argument("--layer-compute-mib", type=int, default=0,
                     help="stand-in for each layer's other compute: a device copy of this many MiB on the "
                          "main stream after every layer (the IndexShare overlap case uses 2048)")
-    ap.add_argument("--measure", default="step", choices=["step", "page_copy"],
-                    help="page_copy: time spill and host import of paged_decode-shaped pages instead of decode steps")
+    ap.add_argument("--measure", default="step", choices=["step", "page_copy", "indexshare_overlap"],
+                    help="page_copy: time spill and host import of paged_decode-shaped pages; "
+                         "indexshare_overlap: the IndexShare step with side-stream replays against inline ones")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -323,24 +517,29 @@ def main():
     if args.measure == "page_copy":
         measure_page_copy(dev, W, args)
         return
+    if args.measure == "indexshare_overlap":
+        measure_indexshare_overlap(dev, W, args)
+        return
     wl = W.WORKLOADS[args.workload]
     total = args.warmup + args.steps
+    n_all = wl.steps if args.all_steps_runs > 0 else 0
+    n_gen = max(total, n_all)
 
     t_setup = time.time()
-    g = GpuRun(wl, total, block_size=args.block_size, replay_grid=args.replay_grid, host_flags=args.host_flags,
+    g = GpuRun(wl, n_gen, block_size=args.block_size, replay_grid=args.replay_grid, host_flags=args.host_flags,
                fuse_backup=not args.no_fuse_backup)
     host_copy = None if args.no_cpu_baseline else [np.array(a, copy=True) for a in g.cache.host_np]
     streams = {a: W.TopkStream(wl, a) for a in wl.anchors}
-    topk_all = [draw_topk(wl, streams, k) for k in range(total)]
+    topk_all = [draw_topk(wl, streams, k) for k in range(n_gen)]
     topk_dev = [{a: torch.from_numpy(v).to(dev) for a, v in t.items()} for t in topk_all]
-    newkv_dev = [new_kv_all_layers(wl, k, dev) for k in range(total)]
-    seq_dev = [g.seq_lens(k) for k in range(total)]
+    newkv_dev = [new_kv_all_layers(wl, k, dev) for k in range(n_gen)]
+    seq_dev = [g.seq_lens(k) for k in range(n_gen)]
     # every step records into its own plan count (pos/slot rows are shared), so
     # nothing but the path runs inside the timed steps
     from decode_memory_tiering_amd.hisparse import Plan
     shared = {a: [Plan.empty(wl.R, wl.K, dev) for _ in range(wl.spec)] for a in wl.anchors}
     step_plans = [{a: [Plan(p.pos, p.slot, torch.zeros(wl.R, dtype=torch.int32, device=dev))
-                       for p in shared[a]] for a in wl.anchors} for _ in range(total)]
+                       for p in shared[a]] for a in wl.anchors} for _ in range(n_gen)]
     torch.cuda.synchronize(dev)
     log(f"[bench] {wl.name}: setup {time.time() - t_setup:.1f}s")
 
@@ -440,14 +639,12 @@ def main():
     mean_launch_s = float(np.mean(launch_ms)) * 1e-3
     miss_bytes_per_launch = misses * wl.rb / n_swap
     achieved = miss_bytes_per_launch / mean_launch_s / 1e9
-    # resolve-pass metadata bytes per launch (top-k read + slot write per entry;
-    # slot map read, LRU read + write per slow row; slot map write + plan pair per miss)
-    slow_rows = 0
     res = W.resident_mask(wl)
-    for k in range(args.warmup, total):
-        L = W.seq_lens_at(wl, k)
-        slow_rows += int(np.count_nonzero((L > wl.B) & (res == 0))) * len(wl.anchors) * wl.spec
-    meta_bytes = entries * 8 + slow_rows * 12 * wl.B + misses * 12 + slow_rows * 4
+    # rows a fused store + backup launch writes to the hot buffer and the host pool
+    fused_rows = args.steps * len(wl.anchors) * int(np.count_nonzero(res == 0)) if g.fuse_backup else 0
+    alg = algorithmic_bytes(wl, topk_all, range(args.warmup, total), misses, fused_rows)
+    meta_bytes = alg["hbm_read"] + alg["hbm_write"] - misses * wl.rb - 2 * fused_rows * wl.rb
+    alg_total = alg["host_link_read"] + alg["host_link_write"] + alg["hbm_read"] + alg["hbm_write"]
 
     def kind_stats(kind, rows_per_run):
         """Host-link rate of one launch kind: rows moved x row bytes / mean launch time."""
@@ -465,6 +662,47 @@ def main():
     # a separate backup launch copies one row per non-resident request (anchor
     # layers' backups ride in their swap-in launch and have no launch of their own)
     backup_rows = len(ev["backup"]) * int(np.count_nonzero(res == 0))
+
+    # The workload's whole decode from admission: the first step finds every
+    # long request's buffer empty (all misses).  Wall clock over all steps,
+    # median of the repetitions; then one more repetition with an event on
+    # the main stream at every step boundary for the per-step times.
+    all_steps = None
+    if n_all:
+        all_walls = []
+        for _ in range(args.all_steps_runs):
+            g.readmit()
+            t0 = time.perf_counter()
+            for k in range(n_all):
+                run(k)
+            torch.cuda.synchronize(dev)
+            all_walls.append(time.perf_counter() - t0)
+        g.readmit()
+        main_s = torch.cuda.current_stream(dev)
+        bounds = [torch.cuda.Event(enable_timing=True) for _ in range(n_all + 1)]
+        bounds[0].record(main_s)
+        for k in range(n_all):
+            run(k)
+            bounds[k + 1].record(main_s)
+        torch.cuda.synchronize(dev)
+        step_ms = [bounds[k].elapsed_time(bounds[k + 1]) for k in range(n_all)]
+        per_k = [sum(int(np.count_nonzero(v >= 0)) for v in topk_all[k].values()) for k in range(n_all)]
+        all_misses = [sum(int(p.count.sum().item()) for a in wl.anchors for p in step_plans[k][a])
+                      for k in range(n_all)]
+        w_all = float(np.median(all_walls))
+        all_steps = dict(
+            steps=n_all, value=sum(per_k) / w_all, ms_per_step=w_all / n_all * 1e3,
+            runs_ms_per_step=[w / n_all * 1e3 for w in all_walls],
+            first_steps_ms=[round(x, 4) for x in step_ms[:4]],
+            first_steps_misses=all_misses[:4],
+            steady_value=sum(per_k[2:]) / (sum(step_ms[2:]) * 1e-3) if n_all > 2 else None,
+            steady_ms_per_step=float(np.mean(step_ms[2:])) if n_all > 2 else None,
+            miss_gbps=sum(all_misses) * wl.rb / w_all / 1e9,
+            note="steps 0..{} of the workload's decode from admission; value by wall clock (median of {} runs); "
+                 "per-step times from events at step boundaries in one more run; steady = steps 2 on"
+                 .format(n_all - 1, args.all_steps_runs))
+        log(f"[bench] all {n_all} steps: {w_all * 1e3:.2f} ms, first step {step_ms[0]:.3f} ms")
+
     err = g.cache.get_error()
     if err:
         log(f"[bench] device error word {err:#x}")
@@ -475,12 +713,16 @@ def main():
     best_link = max(link, zc) if link else None
     cpu = None
     if not args.no_cpu_baseline:
-        newkv_np = [t.cpu().numpy() for t in newkv_dev]
+        newkv_np = [t.cpu().numpy() for t in newkv_dev[:total]]
         g.close()
-        cpu = cpu_baseline(wl, total, args.warmup, host_copy, topk_all, newkv_np)
+        cpu = cpu_baseline(wl, total, args.warmup, host_copy, topk_all, newkv_np, pool_steps=n_gen)
     else:
         g.close()
 
+    cb = counter_bytes(wl.name, args.steps, args.warmup, args.runs)
+    traffic = None if cb is None else cb[0] + cb[1]
+    tr_us = trace_mean_us(wl.name, args.steps, args.warmup, args.runs)
+    step_s = wall / args.steps
     rec = {
         "metric": "top-k rows resolved/s per decode step; miss-copy GB/s as % of host-link peak",
         "value": entries / wall,
@@ -488,7 +730,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall / args.steps * 1e3,
+        "ms_per_step": step_s * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -512,13 +754,21 @@ def main():
             "peak": PCIE5_X16_GBPS,
             "unit": "GB/s",
             "frac": achieved / PCIE5_X16_GBPS,
-            "traffic": counter_traffic(wl.name),
-            # the counters' fetched bytes over the live mean launch time: the
-            # miss copy's read rate as the fabric saw it (metadata included)
-            "counter_fetch_gbps": (counter_bytes(wl.name)[0] / mean_launch_s / 1e9)
-                                  if counter_bytes(wl.name) else None,
+            "traffic": traffic,
+            # counters over the algorithmic bytes of the same launches (1.0 =
+            # no byte moved that the method does not need)
+            "traffic_ratio": traffic / (alg_total / n_swap) if traffic else None,
+            "counter_fetch_bytes": cb[0] if cb else None,
+            "counter_write_bytes": cb[1] if cb else None,
+            "algorithmic_bytes_per_launch": {k: alg[k] / n_swap for k in
+                                             ("host_link_read", "host_link_write", "hbm_read", "hbm_write")},
             "launches": n_swap,
             "mean_launch_us": mean_launch_s * 1e6,
+            "trace_mean_launch_us": tr_us,
+            "achieved_from_trace": miss_bytes_per_launch / (tr_us * 1e-6) / 1e9 if tr_us else None,
+            # a lower bound that needs no per-launch timing: every miss byte of
+            # a step over the whole step's wall time
+            "achieved_from_step_time": miss_bytes_per_launch * per_step["swap_in"] / step_s / 1e9,
             "miss_bytes_per_launch": miss_bytes_per_launch,
             "measured_link_gbps": link,
             "zero_copy_link_gbps": zc,
@@ -529,6 +779,7 @@ def main():
         },
         "runs": {"n": args.runs, "ms_per_step": [w / args.steps * 1e3 for w in walls],
                  "value_min": entries / max(walls), "value_max": entries / min(walls)},
+        "all_steps": all_steps,
         "replay": kind_stats("replay", replay_rows),
         "backup": kind_stats("backup", backup_rows),
         "tiers": tier_shares(wl, topk_all, range(args.warmup, total), misses,

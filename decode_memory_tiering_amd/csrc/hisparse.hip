@@ -32,7 +32,6 @@
 #include <cstdint>
 #include <cstring>
 #include <new>
-#include <vector>
 
 #include "hisparse.h"
 
@@ -43,6 +42,7 @@ constexpr int kMissMark = INT_MIN;   // out_s value of an entry still waiting fo
 constexpr int kMaxB = 16384;
 constexpr int kMaxK = 4096;
 constexpr int kDefaultBlock = 1024;
+constexpr int kMaxLayers = 256;
 constexpr int kDefaultReplayGrid = 12;   // enough to fill the host link without crowding the fabric (measured)
 // Copy-loop shape: batches of kCopyUnroll 16-byte loads per thread, kCopyBuffers
 // batches in rotation (measured on MI355X; see RowCopy).  The swap-in's
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
             const unsigned long long e = (static_cast<unsigned long long>(static_cast<uint32_t>(t)) << 32) |
                                          (static_cast<uint32_t>(i) | (res ? kResidentIdx : 0u));
             uint32_t h = hash_slot(t, a.hash_bits);
-            for (;;) {   // the table has at least 4K entries, so a free one is always reached
+            for (;;) {   // at most K of the table's >= 2K entries are used (load <= 1/2), so a free one is always reached
                 const unsigned long long prev = atomicCAS(&s.hash[h], kHashEmpty, e);
                 if (prev == kHashEmpty) break;
                 if (static_cast<uint32_t>(prev >> 32) == static_cast<uint32_t>(t)) {
@@ -886,6 +886,11 @@ __global__ __launch_bounds__(256) void init_state_kernel(int32_t* lru, int32_t* 
     }
 }
 
+__global__ __launch_bounds__(64) void clear_word_kernel(uint32_t* w)
+{
+    if (threadIdx.x == 0) *w = 0u;
+}
+
 __global__ __launch_bounds__(256) void admit_state_kernel(int32_t* lru, int32_t* tok, const int32_t* req_ids,
                                                           const int32_t* L0s, int R, int B, uint32_t* err)
 {
@@ -972,10 +977,13 @@ struct hisparse_ctx {
     int block = kDefaultBlock, replay_grid = kDefaultReplayGrid, hash_bits = 1;
     size_t lds = 0;
     SwapInFn swap_in_fn = nullptr;
-    std::vector<const uint8_t*> host;   // device-usable address of each layer's host pool
-    std::vector<uint8_t*> hot;
-    std::vector<int32_t> anchor_of;
-    std::vector<int32_t*> lru, tok;     // per layer; null for skip layers
+    // per layer (fixed arrays: a context holds no heap memory beyond itself)
+    const uint8_t* host[kMaxLayers] = {};   // device-usable address of each layer's host pool
+    uint8_t* host_ptr[kMaxLayers] = {};     // the same pool's host address (copy-engine transfers)
+    uint8_t* hot[kMaxLayers] = {};
+    int32_t anchor_of[kMaxLayers] = {};
+    int32_t* lru[kMaxLayers] = {};          // null for skip layers
+    int32_t* tok[kMaxLayers] = {};
     uint32_t* err = nullptr;
 };
 
@@ -1067,13 +1075,17 @@ int hisparse_host_free(void* p)
     return hip_rc(hipHostFree(p));
 }
 
-int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out)
+namespace {
+
+// The checks of the configuration and of the memory it names, the kernel
+// instantiation and its LDS, all filled into *c.  No device memory is
+// allocated here.
+int init_common(const hisparse_config* cfg, hisparse_ctx* c)
 {
-    if (!cfg || !out) return HISPARSE_EINVAL;
-    *out = nullptr;
     const int K = cfg->top_k, B = cfg->device_buffer_size;
     if (K < 1 || B < 1 || K > B || B > kMaxB || K > kMaxK) return HISPARSE_EINVAL;
-    if (cfg->num_layers < 1 || cfg->max_requests < 1 || cfg->max_seq_len < 1) return HISPARSE_EINVAL;
+    if (cfg->num_layers < 1 || cfg->num_layers > kMaxLayers || cfg->max_requests < 1 || cfg->max_seq_len < 1)
+        return HISPARSE_EINVAL;
     if (cfg->row_bytes < 16 || cfg->row_bytes % 16) return HISPARSE_EINVAL;
     if (!cfg->host_pool || !cfg->hot_buffer || !cfg->anchor_of) return HISPARSE_EINVAL;
     int block = cfg->block_size ? cfg->block_size : kDefaultBlock;
@@ -1083,70 +1095,91 @@ int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out)
     const size_t host_bytes = size_t(cfg->max_requests) * cfg->max_seq_len * cfg->row_bytes;
     const size_t hot_bytes = size_t(cfg->max_requests) * (B + 1) * size_t(cfg->row_bytes);
     if (size_t(cfg->max_requests) * cfg->max_seq_len > size_t(INT32_MAX) * 64) return HISPARSE_EINVAL;
+    // the replay stages absolute hot rows r * (B + 1) + slot as int32
+    if (size_t(cfg->max_requests) * (size_t(B) + 1) > size_t(INT32_MAX)) return HISPARSE_EINVAL;
 
-    hisparse_ctx* c = new (std::nothrow) hisparse_ctx;
-    if (!c) return HISPARSE_ENOMEM;
     c->K = K; c->B = B; c->layers = cfg->num_layers; c->R = cfg->max_requests;
     c->max_seq = cfg->max_seq_len; c->rb = cfg->row_bytes;
     c->block = block; c->replay_grid = replay_grid;
-
-    c->anchor_of.assign(cfg->anchor_of, cfg->anchor_of + cfg->num_layers);
-    auto fail = [&](int rc) { hisparse_destroy(c); return rc; };
+    for (int l = 0; l < c->layers; ++l) c->anchor_of[l] = cfg->anchor_of[l];
 
     for (int l = 0; l < c->layers; ++l) {
         const int g = c->anchor_of[l];
-        if (g < 0 || g >= c->layers || c->anchor_of[g] != g) return fail(HISPARSE_EINVAL);
+        if (g < 0 || g >= c->layers || c->anchor_of[g] != g) return HISPARSE_EINVAL;
         void* hp = cfg->host_pool[l];
         void* dp = cfg->hot_buffer[l];
-        if (!hp || !dp || !aligned16(hp) || !aligned16(dp)) return fail(HISPARSE_EINVAL);
+        if (!hp || !dp || !aligned16(hp) || !aligned16(dp)) return HISPARSE_EINVAL;
         const uint8_t* dv = device_view_of_host(hp, host_bytes);
-        if (!dv || !aligned16(dv)) return fail(HISPARSE_EINVAL);
-        if (!is_device_memory(dp, hot_bytes)) return fail(HISPARSE_EINVAL);
-        c->host.push_back(dv);
-        c->hot.push_back(static_cast<uint8_t*>(dp));
+        if (!dv || !aligned16(dv)) return HISPARSE_EINVAL;
+        if (!is_device_memory(dp, hot_bytes)) return HISPARSE_EINVAL;
+        c->host[l] = dv;
+        c->host_ptr[l] = static_cast<uint8_t*>(hp);
+        c->hot[l] = static_cast<uint8_t*>(dp);
     }
-    if (hipGetDevice(&c->device) != hipSuccess) return fail(HISPARSE_EHIP(hipGetLastError()));
+    if (hipGetDevice(&c->device) != hipSuccess) return HISPARSE_EHIP(hipGetLastError());
 
     const int nwaves = block / kWave;
     const int eb = ((B + 63) / 64 + nwaves - 1) / nwaves;
     const int ek = ((K + 63) / 64 + nwaves - 1) / nwaves;
     c->swap_in_fn = pick_kernel(eb, ek);
-    if (!c->swap_in_fn) return fail(HISPARSE_EINVAL);
+    if (!c->swap_in_fn) return HISPARSE_EINVAL;
     int max_lds = 0;
     if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device) != hipSuccess)
-        return fail(HISPARSE_EHIP(hipGetLastError()));
+        return HISPARSE_EHIP(hipGetLastError());
     c->hash_bits = hash_bits_for(K, B, size_t(max_lds));
     c->lds = swap_in_lds_bytes_impl(B, K, c->hash_bits);
-    if (c->lds > size_t(max_lds)) return fail(HISPARSE_EINVAL);
+    if (c->lds > size_t(max_lds)) return HISPARSE_EINVAL;
     const size_t rlds = replay_lds_bytes(c->R) + 16 * sizeof(int);
-    if (rlds > size_t(max_lds)) return fail(HISPARSE_EINVAL);
+    if (rlds > size_t(max_lds)) return HISPARSE_EINVAL;
     if (rlds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&replay_kernel),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(replay_lds_bytes(c->R)));
-        if (e != hipSuccess) return fail(HISPARSE_EHIP(e));
+        if (e != hipSuccess) return HISPARSE_EHIP(e);
     }
     if (c->lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(c->swap_in_fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(c->lds));
-        if (e != hipSuccess) return fail(HISPARSE_EHIP(e));
+        if (e != hipSuccess) return HISPARSE_EHIP(e);
     }
+    return HISPARSE_OK;
+}
 
-    const size_t state_bytes = size_t(c->R) * B * sizeof(int32_t);
-    c->lru.assign(c->layers, nullptr);
-    c->tok.assign(c->layers, nullptr);
+// Every anchor layer's state as if each request were admitted with a prompt
+// longer than B, and a clear error word; on the null stream, then waited for.
+int reset_state(hisparse_ctx* c)
+{
+    for (int l = 0; l < c->layers; ++l) {
+        if (!is_anchor(c, l)) continue;
+        hipLaunchKernelGGL(init_state_kernel, dim3(1024), dim3(256), 0, nullptr, c->lru[l], c->tok[l], c->R, c->B);
+    }
+    hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, nullptr, c->err);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    return hip_rc(e);
+}
+
+}  // namespace
+
+int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out)
+{
+    if (!cfg || !out) return HISPARSE_EINVAL;
+    *out = nullptr;
+    hisparse_ctx* c = new (std::nothrow) hisparse_ctx;
+    if (!c) return HISPARSE_ENOMEM;
+    auto fail = [&](int rc) { hisparse_destroy(c); return rc; };
+    const int rc = init_common(cfg, c);
+    if (rc != HISPARSE_OK) return fail(rc);
+
+    const size_t state_bytes = size_t(c->R) * c->B * sizeof(int32_t);
     for (int l = 0; l < c->layers; ++l) {
         if (!is_anchor(c, l)) continue;   // skip layers share their anchor's state
         hipError_t e1 = hipMalloc(&c->lru[l], state_bytes);
         hipError_t e2 = e1 == hipSuccess ? hipMalloc(&c->tok[l], state_bytes) : e1;
         if (e1 != hipSuccess || e2 != hipSuccess) { (void)hipGetLastError(); return fail(HISPARSE_ENOMEM); }
-        hipLaunchKernelGGL(init_state_kernel, dim3(1024), dim3(256), 0, nullptr, c->lru[l], c->tok[l], c->R, B);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return fail(HISPARSE_EHIP(e));
     }
     if (hipMalloc(&c->err, sizeof(uint32_t)) != hipSuccess) { (void)hipGetLastError(); return fail(HISPARSE_ENOMEM); }
-    hipError_t e = hipMemset(c->err, 0, sizeof(uint32_t));
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) return fail(HISPARSE_EHIP(e));
+    const int rs = reset_state(c);
+    if (rs != HISPARSE_OK) return fail(rs);
     *out = c;
     return HISPARSE_OK;
 }
@@ -1154,8 +1187,10 @@ int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out)
 void hisparse_destroy(hisparse_ctx* c)
 {
     if (!c) return;
-    for (int32_t* p : c->lru) if (p) (void)hipFree(p);
-    for (int32_t* p : c->tok) if (p) (void)hipFree(p);
+    for (int l = 0; l < kMaxLayers; ++l) {
+        if (c->lru[l]) (void)hipFree(c->lru[l]);
+        if (c->tok[l]) (void)hipFree(c->tok[l]);
+    }
     if (c->err) (void)hipFree(c->err);
     delete c;
 }
@@ -1316,6 +1351,76 @@ int launch_page_copy(hisparse_ctx* c, int32_t layer, const void* src, int32_t sr
 }
 
 }  // namespace
+
+namespace {
+
+// Copy-engine form of the page transfers.  The transfer list is host memory
+// (the worker's own list of physical copy coordinates), checked whole before
+// anything is issued; consecutive transfers that are contiguous on every side
+// (same request, next host page, next source page, next mirror page or no
+// mirror, previous page not cut at the pool end) merge into one run, and each
+// run is one asynchronous DMA copy device -> pinned host (plus one device ->
+// device copy into the mirror), so no compute unit moves the bytes.
+int launch_page_copy_dma(hisparse_ctx* c, int32_t layer, const void* src, int32_t src_pages, int32_t page_size,
+                         void* mirror, int32_t mirror_pages, const int32_t* transfers, int32_t n,
+                         hipStream_t stream)
+{
+    if (!usable(c) || layer < 0 || layer >= c->layers || n < 0 || page_size < 1 || src_pages < 0 || mirror_pages < 0)
+        return HISPARSE_EINVAL;
+    if (n == 0) return HISPARSE_OK;
+    if (!src || !transfers || (mirror_pages > 0 && !mirror)) return HISPARSE_EINVAL;
+    const long long P = page_size;
+    for (int32_t x = 0; x < n; ++x) {
+        const int32_t* t = transfers + 4 * size_t(x);
+        const bool ok = t[0] >= 0 && t[0] < src_pages && t[1] >= 0 && t[1] < c->R && t[2] >= 0 &&
+                        t[2] * P < c->max_seq && t[3] >= -1 && t[3] < mirror_pages;
+        if (!ok) return HISPARSE_EINVAL;
+    }
+    const size_t rb = size_t(c->rb);
+    const uint8_t* s8 = static_cast<const uint8_t*>(src);
+    uint8_t* m8 = static_cast<uint8_t*>(mirror);
+    for (int32_t x = 0; x < n;) {
+        const int32_t* t0 = transfers + 4 * size_t(x);
+        long long rows = 0;
+        int32_t y = x;
+        for (;; ++y) {
+            const int32_t* t = transfers + 4 * size_t(y);
+            const long long hp = t[2];
+            const long long page_rows = c->max_seq - hp * P < P ? c->max_seq - hp * P : P;
+            rows += page_rows;
+            if (y + 1 >= n || page_rows < P) break;
+            const int32_t* u = t + 4;
+            const bool mirror_next = t[3] < 0 ? u[3] < 0 : u[3] == t[3] + 1;
+            if (u[1] != t[1] || u[2] != t[2] + 1 || u[0] != t[0] + 1 || !mirror_next) break;
+        }
+        const size_t bytes = size_t(rows) * rb;
+        const uint8_t* from = s8 + size_t(t0[0]) * size_t(P) * rb;
+        uint8_t* to = c->host_ptr[layer] + (size_t(t0[1]) * size_t(c->max_seq) + size_t(t0[2]) * size_t(P)) * rb;
+        hipError_t e = hipMemcpyAsync(to, from, bytes, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess && t0[3] >= 0)
+            e = hipMemcpyAsync(m8 + size_t(t0[3]) * size_t(P) * rb, from, bytes, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return HISPARSE_EHIP(e);
+        x = y + 1;
+    }
+    return HISPARSE_OK;
+}
+
+}  // namespace
+
+int hisparse_spill_dma(hisparse_ctx* c, int32_t layer, const void* resident_cache, int32_t resident_pages,
+                       int32_t page_size, const int32_t* transfers, int32_t n, hipStream_t stream)
+{
+    return launch_page_copy_dma(c, layer, resident_cache, resident_pages, page_size, nullptr, 0, transfers, n,
+                                stream);
+}
+
+int hisparse_import_dma(hisparse_ctx* c, int32_t layer, const void* staging, int32_t staging_pages,
+                        int32_t page_size, void* resident_cache, int32_t resident_pages, const int32_t* transfers,
+                        int32_t n, hipStream_t stream)
+{
+    return launch_page_copy_dma(c, layer, staging, staging_pages, page_size, resident_cache, resident_pages,
+                                transfers, n, stream);
+}
 
 int hisparse_spill(hisparse_ctx* c, int32_t layer, const void* resident_cache, int32_t resident_pages,
                    int32_t page_size, const int32_t* transfers, int32_t n, hipStream_t stream)

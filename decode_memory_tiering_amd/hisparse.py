@@ -38,7 +38,8 @@ EXPORTS = (
     "hisparse_init", "hisparse_destroy", "hisparse_admit", "hisparse_store_newest",
     "hisparse_swap_in", "hisparse_store_swap_in", "hisparse_store_swap_in_backup", "hisparse_swap_in_paged",
     "hisparse_store_swap_in_paged_backup",
-    "hisparse_replay_plan", "hisparse_backup", "hisparse_spill", "hisparse_import", "hisparse_get_state",
+    "hisparse_replay_plan", "hisparse_backup", "hisparse_spill", "hisparse_import", "hisparse_spill_dma",
+    "hisparse_import_dma", "hisparse_get_state",
     "hisparse_set_state", "hisparse_get_error", "hisparse_host_alloc", "hisparse_host_free",
     "hisparse_swap_in_lds_bytes", "hisparse_strerror", "hisparse_version",
 )
@@ -102,6 +103,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hisparse_backup.argtypes = [P, I32, P, P, P, I32, P]
     lib.hisparse_spill.argtypes = [P, I32, P, I32, I32, P, I32, P]
     lib.hisparse_import.argtypes = [P, I32, P, I32, I32, P, I32, P, I32, P]
+    lib.hisparse_spill_dma.argtypes = [P, I32, P, I32, I32, P, I32, P]
+    lib.hisparse_import_dma.argtypes = [P, I32, P, I32, I32, P, I32, P, I32, P]
     lib.hisparse_get_state.argtypes = [P, I32, P, P, P]
     lib.hisparse_set_state.argtypes = [P, I32, P, P, P]
     lib.hisparse_get_error.argtypes = [P, ctypes.POINTER(U32), ctypes.c_int, P]
@@ -270,6 +273,29 @@ def hisparse_import(ctx: int, layer: int, staging, page_size: int, resident_cach
                                   _stream(stream)), "hisparse_import")
 
 
+def _host_transfers(transfers) -> np.ndarray:
+    t = np.ascontiguousarray(np.asarray(transfers, dtype=np.int32).reshape(-1, 4))
+    return t
+
+
+def hisparse_spill_dma(ctx: int, layer: int, resident_cache, page_size: int, transfers, stream=None) -> None:
+    """transfers: host array [n][4] (numpy or CPU tensor)."""
+    pages = int(resident_cache.shape[0]) // page_size
+    t = _host_transfers(transfers)
+    _check(_lib().hisparse_spill_dma(ctx, layer, _ptr(resident_cache), pages, page_size, t.ctypes.data,
+                                     int(t.shape[0]), _stream(stream)), "hisparse_spill_dma")
+
+
+def hisparse_import_dma(ctx: int, layer: int, staging, page_size: int, resident_cache, transfers,
+                        stream=None) -> None:
+    """transfers: host array [n][4] (numpy or CPU tensor)."""
+    rpages = 0 if resident_cache is None else int(resident_cache.shape[0]) // page_size
+    t = _host_transfers(transfers)
+    _check(_lib().hisparse_import_dma(ctx, layer, _ptr(staging), int(staging.shape[0]) // page_size, page_size,
+                                      _ptr(resident_cache), rpages, t.ctypes.data, int(t.shape[0]),
+                                      _stream(stream)), "hisparse_import_dma")
+
+
 def hisparse_get_state(ctx: int, anchor_layer: int, lru, slot_tok, stream=None) -> None:
     _check(_lib().hisparse_get_state(ctx, anchor_layer, _ptr(lru), _ptr(slot_tok), _stream(stream)),
            "hisparse_get_state")
@@ -420,6 +446,12 @@ class HiSparseCache:
 
     def import_pages(self, layer, staging, page_size, resident_cache, transfers, stream=None):
         hisparse_import(self.ctx, layer, staging, page_size, resident_cache, transfers, stream)
+
+    def spill_dma(self, layer, resident_cache, page_size, transfers, stream=None):
+        hisparse_spill_dma(self.ctx, layer, resident_cache, page_size, transfers, stream)
+
+    def import_pages_dma(self, layer, staging, page_size, resident_cache, transfers, stream=None):
+        hisparse_import_dma(self.ctx, layer, staging, page_size, resident_cache, transfers, stream)
 
     def get_state(self, anchor, stream=None):
         import torch

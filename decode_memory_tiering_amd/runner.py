@@ -8,9 +8,14 @@ prefetch"; vLLM design note "HiSparse local KV offload architecture",
   store_newest(l)                        the forward's KV write (on an anchor layer
                                          it rides in the first swap-in's launch)
   anchor layer:  swap_in(l), once per verify row s, each with its own plan row
-                 then, with prefetch on, the replays of its skip layers are
-                 issued on the side stream after an event
-  skip layer:    wait for its replay (prefetch) or replay inline
+                 then, with prefetch on, the replays of verify row 0's plan
+                 on its skip layers are issued on the side stream after an
+                 event
+  skip layer:    per verify row s, in order: the replay of plan row s (row 0
+                 from the side stream when prefetched, else inline), then
+                 that row's consumer.  Row s+1's misses take victims from
+                 slots row s resolved to, so row s+1 is replayed only after
+                 row s was consumed; this is why only row 0 is prefetched.
   backup(l)                              eager backup of the newest token (on an
                                          anchor layer it rides in that launch too)
 
@@ -150,12 +155,14 @@ class GpuRun:
     # -- one decode step ------------------------------------------------------
     def step(self, topk: Dict[int, "torch.Tensor"], new_kv: "torch.Tensor", seq_lens,
              between_layers=None, after_swap_in=None, plans: Optional[Dict[int, List[Plan]]] = None,
-             seq_lens_np=None):
+             seq_lens_np=None, after_replay=None):
         """topk[g]: [S][R][K] int32 (device) for every anchor g; new_kv:
         [layers][R][rb] uint8 (device); seq_lens: [R] int32 (device).
         between_layers(l) runs on the main stream after layer l (a stand-in for
         the layer's other compute); after_swap_in(g, s) runs right after each
-        swap-in (the consumer of that verify row); plans replaces the plan rows
+        swap-in (the consumer of that verify row); after_replay(l, s) runs on
+        the main stream once skip layer l's rows of verify row s are in place
+        (that layer's consumer of the row); plans replaces the plan rows
         this step records into (default: self.plans); seq_lens_np (host copy
         of seq_lens) lets a paged run write the newest token into a resident
         page, as the forward would."""
@@ -193,17 +200,18 @@ class GpuRun:
                     self.side.wait_event(ev)
                     with torch.cuda.stream(self.side):
                         for x in skips:
-                            for s in range(wl.spec):
-                                c.replay_plan(x, plans[l][s], None, self.side)
+                            c.replay_plan(x, plans[l][0], None, self.side)
                             e2 = torch.cuda.Event()
                             e2.record(self.side)
                             self.events[x] = e2
             else:
-                if self.prefetch:
-                    main.wait_event(self.events.pop(l))
-                else:
-                    for s in range(wl.spec):
+                for s in range(wl.spec):
+                    if self.prefetch and s == 0:
+                        main.wait_event(self.events.pop(l))
+                    else:
                         c.replay_plan(l, plans[g][s], None, main)
+                    if after_replay is not None:
+                        after_replay(l, s)
             if not (fused and self.fuse_backup):
                 c.backup(l, seq_lens, self.resident)
             if between_layers is not None:

@@ -38,7 +38,7 @@
  *
  * Every pointer argument of the hot calls (store_newest, swap_in,
  * store_swap_in, store_swap_in_backup, swap_in_paged, replay_plan, backup,
- * spill, import) is device memory unless stated; all of them are
+ * spill, import, spill_dma, import_dma) is device memory unless stated; all of them are
  * asynchronous on the given stream, allocate nothing, never read device data
  * back to the host, and may be captured in a HIP graph.  Ownership: the caller
  * owns host pools, hot buffers, inputs, outputs and plan buffers; the library
@@ -102,7 +102,7 @@ typedef struct hisparse_ctx hisparse_ctx;
 typedef struct {
     int32_t top_k;               /* K, 1 <= K <= B, K <= 4096                       */
     int32_t device_buffer_size;  /* B, 1 <= B <= 16384 (token slots per request)    */
-    int32_t num_layers;          /* layers served by this context                   */
+    int32_t num_layers;          /* layers served by this context, <= 256            */
     int32_t max_requests;        /* R                                               */
     int32_t max_seq_len;         /* host rows per request                           */
     int32_t row_bytes;           /* rb, > 0, multiple of 16                          */
@@ -129,12 +129,15 @@ typedef struct {
 
 /* Create a context: validates the configuration on the host, allocates the
  * LRU state of every anchor layer ([R][B] lru + [R][B] slot map, int32) and
- * the error word on the current device.  State starts as if every request
+ * the error word on the current device.  Besides the limits in
+ * hisparse_config, R * (B + 1) must not exceed INT32_MAX (hot-buffer rows are
+ * 32-bit indices), else HISPARSE_EINVAL.  State starts as if every request
  * had been admitted with a prompt longer than B.  [vLLM] "Main classes"
  * (per-cache runtime owning host/hot views, GPU LRU and the fused resolve). */
 int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out);
 
-/* Free the library-owned state.  Caller-owned memory is untouched. */
+/* Free the library-owned state.  Caller-owned memory is untouched.
+ * Not defined by the pages (library infrastructure). */
 void hisparse_destroy(hisparse_ctx* ctx);
 
 /* A request enters decode with host rows [0, seq_len0) valid (the prefill's
@@ -296,24 +299,56 @@ int hisparse_import(hisparse_ctx* ctx, int32_t layer, const void* staging, int32
                     int32_t page_size, void* resident_cache, int32_t resident_pages,
                     const int32_t* transfers, int32_t n, hipStream_t stream);
 
+/* Copy-engine forms of hisparse_spill and hisparse_import: the same page
+ * transfers, with the same results, moved by the GPU's DMA engines instead of
+ * a kernel, so the transfer occupies no compute unit while the layers' other
+ * work runs ([HiCache] gathers pages with the GPU copy engine rather than SM
+ * kernels; [vLLM] "Spill transaction": the worker enqueues the GPU-to-host
+ * copy from its own list of physical copy coordinates).  Here `transfers` is
+ * HOST memory, [n][4] as above, read during the call.  Consecutive transfers
+ * that are contiguous on every side (same request, next host page, next
+ * source page, next mirror page or none, previous page not cut at
+ * max_seq_len) merge into one copy; each merged run is one asynchronous
+ * device-to-host copy on `stream` (plus one device-to-device copy into the
+ * mirror).  Every transfer is checked before anything is issued: one with a
+ * coordinate out of range makes the call return HISPARSE_EINVAL with nothing
+ * enqueued.  On a HIP error the runs before the failing one stay enqueued.
+ * The caller keeps the host pool reachable by the runtime's copies (memory
+ * from hisparse_host_alloc is). */
+int hisparse_spill_dma(hisparse_ctx* ctx, int32_t layer, const void* resident_cache, int32_t resident_pages,
+                       int32_t page_size, const int32_t* transfers, int32_t n, hipStream_t stream);
+int hisparse_import_dma(hisparse_ctx* ctx, int32_t layer, const void* staging, int32_t staging_pages,
+                        int32_t page_size, void* resident_cache, int32_t resident_pages,
+                        const int32_t* transfers, int32_t n, hipStream_t stream);
+
 /* Copy an anchor layer's state out of / into the library ([R][B] int32 each,
- * device pointers).  For tests and checkpointing; asynchronous on stream. */
+ * device pointers).  For tests and checkpointing; asynchronous on stream.
+ * Not defined by the pages (library infrastructure). */
 int hisparse_get_state(hisparse_ctx* ctx, int32_t anchor_layer, int32_t* lru,
                        int32_t* slot_tok, hipStream_t stream);
 int hisparse_set_state(hisparse_ctx* ctx, int32_t anchor_layer, const int32_t* lru,
                        const int32_t* slot_tok, hipStream_t stream);
 
 /* Read (and optionally clear) the device error word.  Synchronizes the
- * stream: a diagnostic, never part of a decode step. */
+ * stream: a diagnostic, never part of a decode step.  Not defined by the
+ * pages (library infrastructure). */
 int hisparse_get_error(hisparse_ctx* ctx, uint32_t* flags, int clear, hipStream_t stream);
 
-/* Pinned, GPU-mapped host memory for host pools (flags: HISPARSE_HOST_*). */
+/* Pinned, GPU-mapped host memory for host pools (flags: HISPARSE_HOST_*).
+ * The pages have misses copied straight from registered pinned host memory
+ * and give the pinned pool's lifetime to the worker ([vLLM] "Performance
+ * invariants", "Ownership"); this allocator itself is library
+ * infrastructure, not defined by the pages. */
 int hisparse_host_alloc(size_t bytes, uint32_t flags, void** out);
 int hisparse_host_free(void* p);
 
-/* Bytes of LDS one swap-in workgroup uses for this configuration. */
+/* Bytes of LDS one swap-in workgroup uses for this configuration (0 for a
+ * non-positive argument).  Not defined by the pages (library
+ * infrastructure). */
 size_t hisparse_swap_in_lds_bytes(int32_t top_k, int32_t device_buffer_size);
 
+/* Static text for a return code; never NULL.  Version of this ABI.  Not
+ * defined by the pages (library infrastructure). */
 const char* hisparse_strerror(int code);
 int hisparse_version(void);
 

@@ -4,8 +4,9 @@ compare everything, element by element, after every step.
 Compared bit-exactly after every step: the resolved slot ids of every anchor
 layer and verify row, the plan rows (count, then the first count pairs), the
 LRU list and slot map of every request; plus the pages' own correctness
-statement on the GPU's buffers: the row each resolved slot points to holds
-the KV of the position asked for (SGLang guide "Decode Workflow"; vLLM
+statement on the GPU's buffers: for every layer (anchor or skip) and verify
+row, the row each resolved slot points to, read when that layer's consumer
+of the row runs, holds the KV of the position asked for (SGLang guide "Decode Workflow"; vLLM
 design note "Hot lookup and LRU").  At the end: every hot buffer and every
 host pool, byte for byte, and the device error word (must be 0).
 """
@@ -37,7 +38,9 @@ def _eq(name, got, exp):
 def run_lockstep(wl: W.Workload, steps: Optional[int] = None, *, block_size: int = 0, replay_grid: int = 0,
                  prefetch: Optional[bool] = None, compare_state_every: int = 1, check_gather: bool = True,
                  final_bytes: bool = True, progress: bool = False, host_flags: int = 0,
-                 fuse_store: bool = True, fuse_backup: bool = True) -> dict:
+                 fuse_store: bool = True, fuse_backup: bool = True, keep=None) -> dict:
+    """keep: a dict that receives the GPU run's per-step outputs, plan rows and
+    states and its final buffers (to compare two HIP runs with each other)."""
     import torch
     steps = wl.steps if steps is None else steps
     t0 = time.time()
@@ -57,34 +60,57 @@ def run_lockstep(wl: W.Workload, steps: Optional[int] = None, *, block_size: int
         L_np = W.seq_lens_at(wl, k)
         gathered = {}
 
-        def after_swap_in(a, s):
-            if not check_gather:
-                return
+        def gather(layer, a, s):
+            """The rows a consumer of verify row s on `layer` reads: layer's
+            buffer at the slot ids its anchor a resolved."""
             if g.paged:   # rows of the caller's view: resident cache, then hot buffer
-                view = g.row_view(a)
-                gathered[(a, s)] = view[g.out[a][s].clamp(0, view.shape[0] - 1).long().view(-1)].view(R, K, rb)
+                view = g.row_view(layer)
+                gathered[(layer, s)] = view[g.out[a][s].clamp(0, view.shape[0] - 1).long().view(-1)].view(R, K, rb)
                 return
             # Resident rows resolve to positions in the caller's resident cache,
             # not to hot-buffer rows: they are not gathered (index 0 stands in).
             # Slot ids are compared exactly against the oracle elsewhere; the
-            # clamp only keeps this gather inside the buffer.
+            # clamp only keeps this gather inside the buffer (the ids are
+            # checked to lie in [0, B] on the host after the step).
             idx = g.out[a][s].clamp(0, B).long()
             if res_dev is not None:
                 idx = torch.where(res_dev[:, None], torch.zeros_like(idx), idx)
             rows = torch.arange(R, device=dev, dtype=torch.int64)[:, None] * (B + 1) + idx
-            gathered[(a, s)] = g.cache.hot[a].view(R * (B + 1), rb)[rows.view(-1)].view(R, K, rb)
+            gathered[(layer, s)] = g.cache.hot[layer].view(R * (B + 1), rb)[rows.view(-1)].view(R, K, rb)
 
-        g.step(topk_dev, new_kv, g.seq_lens(k), after_swap_in=after_swap_in, seq_lens_np=L_np)
+        def after_swap_in(a, s):
+            if check_gather:
+                gather(a, a, s)
+
+        def after_replay(x, s):
+            # a skip layer's consumer of verify row s reads the anchor's slot ids
+            if check_gather:
+                gather(x, wl.anchor_of[x], s)
+
+        g.step(topk_dev, new_kv, g.seq_lens(k), after_swap_in=after_swap_in, seq_lens_np=L_np,
+               after_replay=after_replay)
         outs, plans = o.step(k, topk, new_kv.cpu().numpy())
         torch.cuda.synchronize(dev)
+        nk_all = new_kv.cpu().numpy()
         for a in wl.anchors:
             for s in range(wl.spec):
                 gout = g.out[a][s].cpu().numpy()
+                if not g.paged:
+                    # the ids the gather used: every valid entry of a non-resident
+                    # row names a row of the request's hot buffer
+                    bad = (topk[a][s] >= 0) & ((gout < 0) | (gout > B)) & (res == 0)[:, None]
+                    if bad.any():
+                        raise Mismatch(f"step {k} layer {a} row {s}: {int(bad.sum())} slot ids outside [0, {B}], "
+                                       f"first at {tuple(np.argwhere(bad)[0])}")
                 _eq(f"step {k} layer {a} row {s} out", gout, outs[a][s])
                 gp, op = g.plans[a][s], plans[a][s]
                 cnt = gp.count.cpu().numpy()
                 _eq(f"step {k} layer {a} row {s} plan count", cnt, op.count)
                 gpos, gslot = gp.pos.cpu().numpy(), gp.slot.cpu().numpy()
+                if keep is not None:
+                    used = np.arange(K)[None, :] < cnt[:, None]        # entries past count are unspecified
+                    keep.setdefault("out", []).append(gout)
+                    keep.setdefault("plan", []).append((cnt, np.where(used, gpos, -7), np.where(used, gslot, -7)))
                 for r in range(R):
                     c = int(cnt[r])
                     if c:
@@ -94,19 +120,24 @@ def run_lockstep(wl: W.Workload, steps: Optional[int] = None, *, block_size: int
                 stats["misses"] += int(cnt.sum())
                 stats["slow_rows"] += int(np.count_nonzero((L_np > B) & (res == 0)))
                 if check_gather:
-                    gat = gathered[(a, s)].cpu().numpy()
-                    host = o.orc.host[a]
-                    nk = new_kv[a].cpu().numpy()
-                    for r in range(R):
-                        if res[r]:
-                            continue
-                        t = topk[a][s][r]
-                        ok = t >= 0
-                        exp = np.where((t == L_np[r] - 1)[:, None], nk[r][None, :], host[r, np.clip(t, 0, None)])
-                        _eq(f"step {k} layer {a} row {s} r {r} gathered rows", gat[r][ok], exp[ok])
+                    # the anchor and each of its skip layers: what that layer's
+                    # consumer of verify row s read is the KV of the positions asked for
+                    for l in (x for x in range(wl.num_layers) if wl.anchor_of[x] == a):
+                        gat = gathered[(l, s)].cpu().numpy()
+                        host = o.orc.host[l]
+                        nk = nk_all[l]
+                        for r in range(R):
+                            if res[r]:
+                                continue
+                            t = topk[a][s][r]
+                            ok = t >= 0
+                            exp = np.where((t == L_np[r] - 1)[:, None], nk[r][None, :], host[r, np.clip(t, 0, None)])
+                            _eq(f"step {k} layer {l} (anchor {a}) row {s} r {r} gathered rows", gat[r][ok], exp[ok])
             if compare_state_every and (k % compare_state_every == 0 or k == steps - 1):
                 lru, tok = g.cache.get_state(a)
                 torch.cuda.synchronize(dev)
+                if keep is not None:
+                    keep.setdefault("state", []).append((lru.cpu().numpy(), tok.cpu().numpy()))
                 _eq(f"step {k} layer {a} lru", lru.cpu().numpy(), o.orc.lru[a])
                 _eq(f"step {k} layer {a} slot map", tok.cpu().numpy(), o.orc.tok[a])
         if progress and (k % 8 == 0 or k == steps - 1):
@@ -115,6 +146,9 @@ def run_lockstep(wl: W.Workload, steps: Optional[int] = None, *, block_size: int
     err = g.cache.get_error()
     if err:
         raise Mismatch(f"device error word {err:#x}")
+    if keep is not None:
+        keep["hot"] = [h.cpu().numpy() for h in g.cache.hot]
+        keep["host"] = [np.array(h, copy=True) for h in g.cache.host_np]
     if final_bytes:
         for l in range(wl.num_layers):
             hot = g.cache.hot[l].cpu().numpy()

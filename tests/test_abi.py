@@ -57,6 +57,7 @@ def test_pure_host_calls(lib):
     dict(num_layers=0),
     dict(block_size=100),
     dict(anchor_of=[1, 0]),                         # anchor of an anchor must be itself
+    dict(max_requests=131072, device_buffer_size=16383),   # R * (B + 1) = 2^31: hot rows overflow int32
 ])
 def test_init_rejects_bad_config_on_host(lib, bad):
     from decode_memory_tiering_amd import hisparse as H

@@ -52,3 +52,31 @@ def test_tier_shares_match_oracle_outputs(wl):
     valid = sum(int((v >= 0).sum()) for t in topk_all for v in t.values())
     assert sum(got["entries"].values()) == valid
     assert 0 < got["hot_hit_rate"] < 1
+
+
+def test_committed_counters_apply_only_to_their_window(tmp_path, monkeypatch):
+    # a counter summary is attached only to the exact decode window (workload,
+    # timed steps, warm-up steps, runs) and kernel source it was taken on
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "swap_in_kernel_wl_counters.md").write_text(
+        "# counters\n\nrocprofv3 --pmc FETCH_SIZE -- python bench.py\n\nsrc_sha256: abc\nworkload: wl\n"
+        "steps: 20\nwarmup: 5\nruns: 5\nfetch_bytes_per_launch: 100\nwrite_bytes_per_launch: 50\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "_src_sha256", lambda: "abc")
+    assert bench.counter_bytes("wl", 20, 5, 5) == (100.0, 50.0)
+    assert bench.counter_bytes("wl", 30, 2, 5) is None        # another window
+    assert bench.counter_bytes("wl", 20, 5, 3) is None
+    assert bench.counter_bytes("other", 20, 5, 5) is None
+    monkeypatch.setattr(bench, "_src_sha256", lambda: "changed")
+    assert bench.counter_bytes("wl", 20, 5, 5) is None        # kernel changed since
+
+
+def test_algorithmic_bytes_split():
+    wl = CASES[0]
+    streams = {a: W.TopkStream(wl, a) for a in wl.anchors}
+    topk_all = [draw_topk(wl, streams, k) for k in range(3)]
+    alg = bench.algorithmic_bytes(wl, topk_all, range(3), misses=10, fused_rows=4)
+    assert alg["host_link_read"] == 10 * wl.rb and alg["host_link_write"] == 4 * wl.rb
+    entries = sum(int((v >= 0).sum()) for t in topk_all for v in t.values())
+    assert alg["entries"] == entries
+    assert alg["hbm_read"] == entries * 4 + alg["slow_rows"] * 8 * wl.B + 4 * wl.rb

@@ -337,6 +337,60 @@ def test_page_copy_parity():
     c.close()
 
 
+def test_page_copy_dma_parity():
+    """The copy-engine spill and import against the oracle and against the
+    kernel forms: scattered pages, runs contiguous on every side (merged into
+    one copy each), a page cut at the pool end, mirrors; a bad transfer
+    anywhere in the list fails the call with nothing enqueued."""
+    R, B, K, rb, P = 4, 64, 24, 48, 16
+    max_seq = 200                                  # last page (12) holds 8 rows
+    rng = np.random.default_rng(7)
+    res = rng.integers(0, 256, size=(20 * P, rb), dtype=np.uint8)
+    stg = rng.integers(0, 256, size=(14 * P, rb), dtype=np.uint8)
+    # spill: scattered, a cut page, a run of three (request 1, host pages 2-4
+    # from resident pages 4-6), a run broken by a source gap
+    spill = np.array([(3, 0, 0, -1), (7, 1, 12, -1), (0, 3, 5, -1), (19, 2, 1, -1),
+                      (4, 1, 2, -1), (5, 1, 3, -1), (6, 1, 4, -1), (10, 2, 5, -1), (12, 2, 6, -1)], np.int32)
+    # import: mirrored and unmirrored runs, a cut page, a run broken by its mirror
+    imp = np.array([(0, 0, 3, 4), (9, 2, 12, -1), (5, 1, 7, 19), (1, 3, 0, -1), (2, 3, 1, -1),
+                    (10, 0, 8, 10), (11, 0, 9, 11), (12, 0, 10, 15), (13, 0, 11, -1)], np.int32)
+    forms = {}
+    o = None
+    for form in ("dma", "kernel"):
+        c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
+        o = o or _oracle_for(c)               # both caches start from the same host pool
+        res_d, stg_d = _dev(res, torch.uint8), _dev(stg, torch.uint8)
+        mirror_d = torch.zeros(20 * P, rb, dtype=torch.uint8, device="cuda")
+        if form == "dma":
+            c.spill_dma(0, res_d, P, spill)
+            c.import_pages_dma(0, stg_d, P, mirror_d, imp)
+        else:
+            c.spill(0, res_d, P, _dev(spill))
+            c.import_pages(0, stg_d, P, mirror_d, _dev(imp))
+        torch.cuda.synchronize()
+        assert c.get_error() == 0
+        forms[form] = (c, mirror_d.cpu().numpy())
+    c, mirror = forms["dma"]
+    mirror_np = np.zeros((20 * P, rb), np.uint8)
+    o.page_copy(0, P, res, spill)
+    o.page_copy(0, P, stg, imp, mirror=mirror_np)
+    assert np.array_equal(c.host_np[0], o.host[0])
+    assert np.array_equal(mirror, mirror_np)
+    assert np.array_equal(forms["kernel"][0].host_np[0], o.host[0])
+    assert np.array_equal(forms["kernel"][1], mirror_np)
+    host0 = c.host_np[0].copy()
+    for bad in ([(0, 0, 6, -1), (20, 0, 0, -1)], [(0, R, 0, -1)], [(0, 0, 13, -1)], [(1, 0, 0, 20)],
+                [(0, 0, -1, -1)], [(-1, 0, 0, -1)], [(0, 0, 0, -2)]):
+        with pytest.raises(H.HisparseError) as e:
+            c.import_pages_dma(0, _dev(stg, torch.uint8), P, torch.zeros(20 * P, rb, dtype=torch.uint8,
+                                                                         device="cuda"), np.array(bad, np.int32))
+        assert e.value.rc == H.HISPARSE_EINVAL
+    torch.cuda.synchronize()
+    assert np.array_equal(c.host_np[0], host0)
+    for cc, _ in forms.values():
+        cc.close()
+
+
 def test_spill_mid_decode_round_trip():
     """A paged decode on GPU and oracle side by side; halfway, half of the
     resident pages are spilled and become host-backed; every output, state,

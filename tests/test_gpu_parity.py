@@ -89,11 +89,24 @@ def _launch_shape_fits(wl, block):
     return _cdiv(_cdiv(wl.B, 64), waves) <= 16 and _cdiv(_cdiv(wl.K, 64), waves) <= 4
 
 
+def _assert_init_rejects(wl, block):
+    """A workgroup too narrow for the buffer (more 64-entry chunks per wave
+    than the kernel holds in registers): init refuses it on the host."""
+    from decode_memory_tiering_amd.hisparse import HISPARSE_EINVAL, HiSparseCache, HisparseError
+    print(f"\n[parity] {wl.name} B={wl.B} K={wl.K} block={block}: init must return EINVAL", flush=True)
+    with pytest.raises(HisparseError) as e:
+        c = HiSparseCache(num_layers=wl.num_layers, anchor_of=wl.anchor_of, R=wl.R, B=wl.B, K=wl.K, rb=wl.rb,
+                          max_seq=W.max_seq(wl), block_size=block)
+        c.close()
+    assert e.value.rc == HISPARSE_EINVAL
+
+
 @pytest.mark.parametrize("block", [128, 256, 1024])
 @pytest.mark.parametrize("wl", RAGGED, ids=[w.name for w in RAGGED])
 def test_ragged_geometries(wl, block):
     if not _launch_shape_fits(wl, block):
-        pytest.skip("buffer too large for this workgroup size (init rejects it)")
+        _assert_init_rejects(wl, block)
+        return
     _lockstep(wl, block_size=block)
 
 

@@ -72,3 +72,26 @@ def test_readmit_repeats_the_decode():
     for x, y in zip(first, again):
         for g in wl.anchors:
             np.testing.assert_array_equal(x[g], y[g])
+
+
+@pytest.mark.parametrize("threads", [1, 3, 16])
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_threaded_timing_driver_runs_the_same_decode(wl, threads):
+    # the CPU baseline's C driver (admission, warm-up steps, timed steps over
+    # request shares on threads) leaves every buffer as the step-by-step
+    # decode does; a second call (re-admitted) repeats it
+    from oracle.timing import DecodeTimer
+    topk, newkv = inputs(wl)
+    ref = OracleRun(wl)
+    for k in range(wl.steps):
+        ref.step(k, topk[k], newkv[k])
+    timed = OracleRun(wl)
+    timer = DecodeTimer(timed, topk, newkv, first_timed=2)
+    for _ in range(2):
+        assert timer.run(threads) >= 0.0
+        a, b = snapshot(ref), snapshot(timed)
+        for x, y in zip(a[0] + a[1], b[0] + b[1]):
+            np.testing.assert_array_equal(x, y)
+        for g in wl.anchors:
+            np.testing.assert_array_equal(a[2][g], b[2][g])
+            np.testing.assert_array_equal(a[3][g], b[3][g])
