@@ -31,6 +31,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "hisparse.h"
@@ -985,6 +986,7 @@ struct hisparse_ctx {
     int32_t* lru[kMaxLayers] = {};          // null for skip layers
     int32_t* tok[kMaxLayers] = {};
     uint32_t* err = nullptr;
+    bool in_scratch = false;                // state lives in the static scratch array (hisparse_init_static)
 };
 
 namespace {
@@ -1033,7 +1035,38 @@ bool is_anchor(const hisparse_ctx* c, int32_t l)
     return l >= 0 && l < c->layers && c->anchor_of[l] == l;
 }
 
+// hisparse_init_static keeps the library-owned device memory of one context
+// per device (each anchor layer's LRU list and slot map, and the error word)
+// in the file-scope array `scratch` below instead of memory from hipMalloc,
+// and the context object itself in a static slot, so that call allocates
+// nothing.  In host code the array's name only stands for the symbol: its
+// address on a device is looked up once, with that device current
+// (hipGetSymbolAddress), kept in the device's slot, and only that address is
+// used.
+constexpr size_t kScratchBytes = size_t(32) << 20;   // 32 MiB per device, held until the process ends
+constexpr size_t kScratchAlign = 256;
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+    uint8_t* ptr = nullptr;   // device address of `scratch` on this device, once looked up
+    bool busy = false;        // a live context of hisparse_init_static uses it
+    hisparse_ctx ctx;         // that context
+};
+ScratchSlot g_slots[kMaxDevices];
+std::mutex g_slots_mu;
+
+size_t scratch_align(size_t x) { return (x + kScratchAlign - 1) & ~(kScratchAlign - 1); }
+
+void release_static(hisparse_ctx* c)
+{
+    std::lock_guard<std::mutex> lk(g_slots_mu);
+    for (ScratchSlot& s : g_slots)
+        if (&s.ctx == c) s.busy = false;
+}
+
 }  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 extern "C" {
 
@@ -1051,6 +1084,8 @@ const char* hisparse_strerror(int code)
     if (code == HISPARSE_OK) return "ok";
     if (code == HISPARSE_EINVAL) return "invalid argument";
     if (code == HISPARSE_ENOMEM) return "out of memory";
+    if (code == HISPARSE_EBUSY) return "the device's static scratch is in use by another context";
+    if (code == HISPARSE_ENOSPC) return "the configuration's state does not fit the static scratch array";
     if (code <= -1000) return hipGetErrorString(static_cast<hipError_t>(-code - 1000));
     return "unknown error";
 }
@@ -1077,9 +1112,9 @@ int hisparse_host_free(void* p)
 
 namespace {
 
-// The checks of the configuration and of the memory it names, the kernel
-// instantiation and its LDS, all filled into *c.  No device memory is
-// allocated here.
+// Everything hisparse_init and hisparse_init_static share: the checks of the
+// configuration and of the memory it names, the kernel instantiation and its
+// LDS, all filled into *c.  No device memory is allocated here.
 int init_common(const hisparse_config* cfg, hisparse_ctx* c)
 {
     const int K = cfg->top_k, B = cfg->device_buffer_size;
@@ -1184,9 +1219,60 @@ int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out)
     return HISPARSE_OK;
 }
 
+int hisparse_init_static(const hisparse_config* cfg, hisparse_ctx** out)
+{
+    if (!cfg || !out) return HISPARSE_EINVAL;
+    *out = nullptr;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return HISPARSE_EHIP(hipGetLastError());
+    if (dev < 0 || dev >= kMaxDevices) return HISPARSE_EINVAL;
+    std::lock_guard<std::mutex> lk(g_slots_mu);
+    ScratchSlot& slot = g_slots[dev];
+    if (slot.busy) return HISPARSE_EBUSY;
+    if (!slot.ptr) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) { (void)hipGetLastError(); return HISPARSE_EHIP(e); }
+        if (!p) return HISPARSE_EHIP(hipErrorInvalidSymbol);
+        slot.ptr = static_cast<uint8_t*>(p);
+    }
+    hisparse_ctx* c = &slot.ctx;
+    *c = hisparse_ctx{};
+    int rc = init_common(cfg, c);
+    if (rc != HISPARSE_OK) return rc;
+    // layout: error word, then each anchor layer's lru and slot map
+    const size_t state = scratch_align(size_t(c->R) * c->B * sizeof(int32_t));
+    size_t need = kScratchAlign;
+    for (int l = 0; l < c->layers; ++l)
+        if (is_anchor(c, l)) need += 2 * state;
+    if (need > kScratchBytes) return HISPARSE_ENOSPC;
+    uint8_t* p = slot.ptr;
+    c->err = reinterpret_cast<uint32_t*>(p);
+    p += kScratchAlign;
+    for (int l = 0; l < c->layers; ++l) {
+        if (!is_anchor(c, l)) continue;
+        c->lru[l] = reinterpret_cast<int32_t*>(p);
+        p += state;
+        c->tok[l] = reinterpret_cast<int32_t*>(p);
+        p += state;
+    }
+    c->in_scratch = true;
+    rc = reset_state(c);   // the array keeps the last context's contents: every byte used is written here
+    if (rc != HISPARSE_OK) return rc;
+    slot.busy = true;
+    *out = c;
+    return HISPARSE_OK;
+}
+
+size_t hisparse_static_scratch_bytes(void) { return kScratchBytes; }
+
 void hisparse_destroy(hisparse_ctx* c)
 {
     if (!c) return;
+    if (c->in_scratch) {   // hisparse_init_static: nothing to free, the device's scratch is released
+        release_static(c);
+        return;
+    }
     for (int l = 0; l < kMaxLayers; ++l) {
         if (c->lru[l]) (void)hipFree(c->lru[l]);
         if (c->tok[l]) (void)hipFree(c->tok[l]);

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(PKG, "libhisparse.so")
 HISPARSE_OK = 0
 HISPARSE_EINVAL = -22
 HISPARSE_ENOMEM = -12
+HISPARSE_EBUSY = -16
+HISPARSE_ENOSPC = -28
 
 HISPARSE_DERR_TOPK_RANGE = 0x1
 HISPARSE_DERR_TOPK_DUP = 0x2
@@ -35,7 +37,8 @@ HISPARSE_HOST_NONCOHERENT = 2
 
 # every entry point include/hisparse.h declares
 EXPORTS = (
-    "hisparse_init", "hisparse_destroy", "hisparse_admit", "hisparse_store_newest",
+    "hisparse_init", "hisparse_init_static", "hisparse_static_scratch_bytes", "hisparse_destroy",
+    "hisparse_admit", "hisparse_store_newest",
     "hisparse_swap_in", "hisparse_store_swap_in", "hisparse_store_swap_in_backup", "hisparse_swap_in_paged",
     "hisparse_store_swap_in_paged_backup",
     "hisparse_replay_plan", "hisparse_backup", "hisparse_spill", "hisparse_import", "hisparse_spill_dma",
@@ -89,6 +92,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I32, U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32
     lib.hisparse_init.argtypes = [ctypes.POINTER(hisparse_config), ctypes.POINTER(ctypes.c_void_p)]
+    lib.hisparse_init_static.argtypes = [ctypes.POINTER(hisparse_config), ctypes.POINTER(ctypes.c_void_p)]
+    lib.hisparse_static_scratch_bytes.argtypes = []
+    lib.hisparse_static_scratch_bytes.restype = ctypes.c_size_t
     lib.hisparse_destroy.argtypes = [P]
     lib.hisparse_destroy.restype = None
     lib.hisparse_admit.argtypes = [P, I32, P, P, I32, P]
@@ -117,7 +123,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hisparse_version.argtypes = []
     for name in EXPORTS:
         fn = getattr(lib, name)
-        if name not in ("hisparse_destroy", "hisparse_strerror", "hisparse_swap_in_lds_bytes"):
+        if name not in ("hisparse_destroy", "hisparse_strerror", "hisparse_swap_in_lds_bytes",
+                        "hisparse_static_scratch_bytes"):
             fn.restype = ctypes.c_int
     return lib
 
@@ -179,7 +186,10 @@ def hisparse_host_free(ptr: int) -> None:
 
 def hisparse_init(*, top_k: int, device_buffer_size: int, num_layers: int, max_requests: int,
                   max_seq_len: int, row_bytes: int, host_pool: Sequence[int], hot_buffer: Sequence,
-                  anchor_of: Sequence[int], block_size: int = 0, replay_grid: int = 0) -> int:
+                  anchor_of: Sequence[int], block_size: int = 0, replay_grid: int = 0,
+                  static_state: bool = False) -> int:
+    """static_state: hisparse_init_static (state in the library's static
+    scratch array, no allocation) instead of hisparse_init."""
     hp = (ctypes.c_void_p * len(host_pool))(*[int(p) for p in host_pool])
     hb = (ctypes.c_void_p * len(hot_buffer))(*[_ptr(t) for t in hot_buffer])
     an = (ctypes.c_int32 * len(anchor_of))(*[int(a) for a in anchor_of])
@@ -188,8 +198,13 @@ def hisparse_init(*, top_k: int, device_buffer_size: int, num_layers: int, max_r
                           ctypes.cast(hb, ctypes.POINTER(ctypes.c_void_p)),
                           ctypes.cast(an, ctypes.POINTER(ctypes.c_int32)), block_size, replay_grid)
     ctx = ctypes.c_void_p()
-    _check(_lib().hisparse_init(ctypes.byref(cfg), ctypes.byref(ctx)), "hisparse_init")
+    name = "hisparse_init_static" if static_state else "hisparse_init"
+    _check(getattr(_lib(), name)(ctypes.byref(cfg), ctypes.byref(ctx)), name)
     return int(ctx.value)
+
+
+def hisparse_static_scratch_bytes() -> int:
+    return int(_lib().hisparse_static_scratch_bytes())
 
 
 def hisparse_destroy(ctx: int) -> None:
@@ -371,7 +386,7 @@ class HiSparseCache:
 
     def __init__(self, *, num_layers: int, anchor_of: Sequence[int], R: int, B: int, K: int, rb: int,
                  max_seq: int, device="cuda", host_flags: int = HISPARSE_HOST_DEFAULT,
-                 block_size: int = 0, replay_grid: int = 0):
+                 block_size: int = 0, replay_grid: int = 0, static_state: bool = False):
         import torch
         self.num_layers, self.R, self.B, self.K, self.rb, self.max_seq = num_layers, R, B, K, rb, max_seq
         self.anchor_of = [int(a) for a in anchor_of]
@@ -388,7 +403,7 @@ class HiSparseCache:
         self.ctx = hisparse_init(top_k=K, device_buffer_size=B, num_layers=num_layers, max_requests=R,
                                  max_seq_len=max_seq, row_bytes=rb, host_pool=self._host_ptrs,
                                  hot_buffer=self.hot, anchor_of=self.anchor_of, block_size=block_size,
-                                 replay_grid=replay_grid)
+                                 replay_grid=replay_grid, static_state=static_state)
 
     def close(self):
         if self.ctx:

@@ -43,7 +43,7 @@ class GpuRun:
     def __init__(self, wl: W.Workload, steps: Optional[int] = None, device: str = "cuda",
                  block_size: int = 0, replay_grid: int = 0, host_flags: int = HISPARSE_HOST_DEFAULT,
                  prefetch: Optional[bool] = None, fill: bool = True, fuse_store: bool = True,
-                 fuse_backup: bool = True):
+                 fuse_backup: bool = True, static_state: bool = False):
         import torch
         self.torch = torch
         self.wl = wl
@@ -54,7 +54,7 @@ class GpuRun:
         self.cache = HiSparseCache(num_layers=wl.num_layers, anchor_of=wl.anchor_of, R=wl.R, B=wl.B,
                                    K=wl.K, rb=wl.rb, max_seq=self.max_seq, device=device,
                                    host_flags=host_flags, block_size=block_size,
-                                   replay_grid=replay_grid)
+                                   replay_grid=replay_grid, static_state=static_state)
         self.prefetch = prefetch_enabled() if prefetch is None else prefetch
         # an anchor layer's KV write rides in its swap-in launch
         # (store_swap_in), and so does its eager backup (store_swap_in_backup)

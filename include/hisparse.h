@@ -80,6 +80,8 @@ extern "C" {
 #define HISPARSE_OK 0
 #define HISPARSE_EINVAL (-22)
 #define HISPARSE_ENOMEM (-12)
+#define HISPARSE_EBUSY (-16)    /* hisparse_init_static: the device's scratch is in use */
+#define HISPARSE_ENOSPC (-28)   /* hisparse_init_static: state larger than the scratch array */
 #define HISPARSE_EHIP(e) (-(1000 + (int)(e)))
 
 /* Device error word bits (hisparse_get_error). */
@@ -135,6 +137,26 @@ typedef struct {
  * had been admitted with a prompt longer than B.  [vLLM] "Main classes"
  * (per-cache runtime owning host/hot views, GPU LRU and the fused resolve). */
 int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * it): hisparse_init with no allocation at all.  The library-owned device
+ * memory (every anchor layer's [R][B] lru and slot map, the error word) is
+ * carved from one static array of the library, hisparse_static_scratch_bytes()
+ * = 32 MiB, which each device the library runs on holds until the process
+ * ends; the context object is a static slot of that device.  The state needs
+ * 256 + 2 * ceil256(R * B * 4) bytes per anchor layer; a configuration that
+ * does not fit returns HISPARSE_ENOSPC.  One such context per device at a
+ * time: while one is live (until hisparse_destroy), another call on that
+ * device returns HISPARSE_EBUSY.  The array keeps the previous context's
+ * contents, so this call writes every byte the new context uses (state as
+ * after hisparse_init, error word 0), on the null stream, and waits for it.
+ * Checks, limits and error codes are otherwise those of hisparse_init, and
+ * every other call works on the context exactly as on one from
+ * hisparse_init; calls on it follow the same ordering rules (calls that
+ * overlap on one anchor layer's state race). */
+int hisparse_init_static(const hisparse_config* cfg, hisparse_ctx** out);
+size_t hisparse_static_scratch_bytes(void);
 
 /* Free the library-owned state.  Caller-owned memory is untouched.
  * Not defined by the pages (library infrastructure). */

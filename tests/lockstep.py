@@ -38,14 +38,15 @@ def _eq(name, got, exp):
 def run_lockstep(wl: W.Workload, steps: Optional[int] = None, *, block_size: int = 0, replay_grid: int = 0,
                  prefetch: Optional[bool] = None, compare_state_every: int = 1, check_gather: bool = True,
                  final_bytes: bool = True, progress: bool = False, host_flags: int = 0,
-                 fuse_store: bool = True, fuse_backup: bool = True, keep=None) -> dict:
+                 fuse_store: bool = True, fuse_backup: bool = True, static_state: bool = False,
+                 keep=None) -> dict:
     """keep: a dict that receives the GPU run's per-step outputs, plan rows and
     states and its final buffers (to compare two HIP runs with each other)."""
     import torch
     steps = wl.steps if steps is None else steps
     t0 = time.time()
     g = GpuRun(wl, steps, block_size=block_size, replay_grid=replay_grid, prefetch=prefetch,
-               host_flags=host_flags, fuse_store=fuse_store, fuse_backup=fuse_backup)
+               host_flags=host_flags, fuse_store=fuse_store, fuse_backup=fuse_backup, static_state=static_state)
     o = OracleRun(wl, steps, host_pools=g.cache.host_np)
     streams = {a: W.TopkStream(wl, a) for a in wl.anchors}
     dev = g.dev
