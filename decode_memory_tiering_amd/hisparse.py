@@ -89,6 +89,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built: run `python -m decode_memory_tiering_amd.build` "
                            "(the HiSparse path has no fallback)")
+    # torch first: its HIP runtime must be the one the library binds to (both
+    # carry the same soname, and the first one loaded serves the process)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I32, U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32
     lib.hisparse_init.argtypes = [ctypes.POINTER(hisparse_config), ctypes.POINTER(ctypes.c_void_p)]
