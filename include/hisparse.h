@@ -151,10 +151,11 @@ int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out);
  * device returns HISPARSE_EBUSY.  The array keeps the previous context's
  * contents, so this call writes every byte the new context uses (state as
  * after hisparse_init, error word 0), on the null stream, and waits for it.
- * Checks, limits and error codes are otherwise those of hisparse_init, and
- * every other call works on the context exactly as on one from
- * hisparse_init; calls on it follow the same ordering rules (calls that
- * overlap on one anchor layer's state race). */
+ * Like hisparse_init it is a set-up call, made before any capture: it
+ * launches on the null stream and waits.  Checks, limits and error codes are
+ * otherwise those of hisparse_init, and every other call works on the
+ * context exactly as on one from hisparse_init; calls on it follow the same
+ * ordering rules (calls that overlap on one anchor layer's state race). */
 int hisparse_init_static(const hisparse_config* cfg, hisparse_ctx** out);
 size_t hisparse_static_scratch_bytes(void);
 
