@@ -252,8 +252,8 @@ def measure_page_copy(dev, W, args):
     """Spill (resident page -> host page) and host import (staging page ->
     host page, half mirrored to resident pages) on the paged decode's shape:
     64-token pages of 1152-byte rows, 4096 pages per call, by the copy kernel
-    and by the copy engines (one DMA copy per run of pages contiguous on both
-    sides).  Two transfer lists: pages scattered over the pool (every page its
+    and by runtime copies (one hipMemcpyAsync per run of pages contiguous on
+    both sides).  Two transfer lists: pages scattered over the pool (every page its
     own copy) and whole runs of 64 consecutive pages (64 copies per call).
     Then each spill form beside a 2 GiB device-to-device copy on another
     stream (a stand-in for a layer's other work): how much the spill slows
@@ -769,9 +769,10 @@ def main():
             "mean_launch_us": mean_launch_s * 1e6,
             "trace_mean_launch_us": tr_us,
             "achieved_from_trace": miss_bytes_per_launch / (tr_us * 1e-6) / 1e9 if tr_us else None,
-            # a lower bound that needs no per-launch timing: every miss byte of
-            # a step over the whole step's wall time
-            "achieved_from_step_time": miss_bytes_per_launch * per_step["swap_in"] / step_s / 1e9,
+            # a lower bound that needs no per-launch timing: every row a step
+            # reads over the host link (misses and skip-layer replays) over
+            # the whole step's wall time
+            "achieved_from_step_time": (misses + replay_rows) * wl.rb / args.steps / step_s / 1e9,
             "miss_bytes_per_launch": miss_bytes_per_launch,
             "measured_link_gbps": link,
             "zero_copy_link_gbps": zc,

@@ -983,7 +983,7 @@ struct hisparse_ctx {
     SwapInFn swap_in_fn = nullptr;
     // per layer (fixed arrays: a context holds no heap memory beyond itself)
     const uint8_t* host[kMaxLayers] = {};   // device-usable address of each layer's host pool
-    uint8_t* host_ptr[kMaxLayers] = {};     // the same pool's host address (copy-engine transfers)
+    uint8_t* host_ptr[kMaxLayers] = {};     // the same pool's host address (runtime-copy transfers)
     uint8_t* hot[kMaxLayers] = {};
     int32_t anchor_of[kMaxLayers] = {};
     int32_t* lru[kMaxLayers] = {};          // null for skip layers
@@ -1448,13 +1448,13 @@ int launch_page_copy(hisparse_ctx* c, int32_t layer, const void* src, int32_t sr
 
 namespace {
 
-// Copy-engine form of the page transfers.  The transfer list is host memory
+// Runtime-copy form of the page transfers.  The transfer list is host memory
 // (the worker's own list of physical copy coordinates), checked whole before
 // anything is issued; consecutive transfers that are contiguous on every side
 // (same request, next host page, next source page, next mirror page or no
 // mirror, previous page not cut at the pool end) merge into one run, and each
-// run is one asynchronous DMA copy device -> pinned host (plus one device ->
-// device copy into the mirror), so no compute unit moves the bytes.
+// run is one asynchronous runtime copy device -> pinned host (plus one device
+// -> device copy into the mirror), with no kernel of this library.
 int launch_page_copy_dma(hisparse_ctx* c, int32_t layer, const void* src, int32_t src_pages, int32_t page_size,
                          void* mirror, int32_t mirror_pages, const int32_t* transfers, int32_t n,
                          hipStream_t stream)
@@ -1490,14 +1490,11 @@ int launch_page_copy_dma(hisparse_ctx* c, int32_t layer, const void* src, int32_
         const size_t bytes = size_t(rows) * rb;
         const uint8_t* from = s8 + size_t(t0[0]) * size_t(P) * rb;
         uint8_t* to = c->host_ptr[layer] + (size_t(t0[1]) * size_t(c->max_seq) + size_t(t0[2]) * size_t(P)) * rb;
-        // The NoCU kind keeps each copy on a DMA engine: a plain device-to-host
-        // copy may be carried out by a blit kernel on the compute units.  The
-        // pinned host pool is mapped into the device's address space, so it is
-        // a valid destination for a device-side copy.
-        hipError_t e = hipMemcpyAsync(to, from, bytes, hipMemcpyDeviceToDeviceNoCU, stream);
+        // Which engine carries the copy (an SDMA engine or the runtime's own
+        // blit kernel) is the HIP runtime's choice.
+        hipError_t e = hipMemcpyAsync(to, from, bytes, hipMemcpyDeviceToHost, stream);
         if (e == hipSuccess && t0[3] >= 0)
-            e = hipMemcpyAsync(m8 + size_t(t0[3]) * size_t(P) * rb, from, bytes, hipMemcpyDeviceToDeviceNoCU,
-                               stream);
+            e = hipMemcpyAsync(m8 + size_t(t0[3]) * size_t(P) * rb, from, bytes, hipMemcpyDeviceToDevice, stream);
         if (e != hipSuccess) return HISPARSE_EHIP(e);
         x = y + 1;
     }

@@ -322,17 +322,19 @@ int hisparse_import(hisparse_ctx* ctx, int32_t layer, const void* staging, int32
                     int32_t page_size, void* resident_cache, int32_t resident_pages,
                     const int32_t* transfers, int32_t n, hipStream_t stream);
 
-/* Copy-engine forms of hisparse_spill and hisparse_import: the same page
- * transfers, with the same results, moved by the GPU's DMA engines instead of
- * a kernel, so the transfer occupies no compute unit while the layers' other
- * work runs ([HiCache] gathers pages with the GPU copy engine rather than SM
- * kernels; [vLLM] "Spill transaction": the worker enqueues the GPU-to-host
- * copy from its own list of physical copy coordinates).  Here `transfers` is
+/* Runtime-copy forms of hisparse_spill and hisparse_import: the same page
+ * transfers, with the same results, handed to the HIP runtime as
+ * asynchronous copies instead of a kernel of this library, for transfers
+ * that run beside other work ([HiCache] gathers pages with the GPU copy
+ * engine rather than SM kernels; [vLLM] "Spill transaction": the worker
+ * enqueues the GPU-to-host copy from its own list of physical copy
+ * coordinates).  Which engine carries each copy (an SDMA engine, or the
+ * runtime's own blit kernel) is the runtime's choice.  Here `transfers` is
  * HOST memory, [n][4] as above, read during the call.  Consecutive transfers
  * that are contiguous on every side (same request, next host page, next
  * source page, next mirror page or none, previous page not cut at
- * max_seq_len) merge into one copy; each merged run is one asynchronous
- * device-to-host copy on `stream` (plus one device-to-device copy into the
+ * max_seq_len) merge into one copy; each merged run is one hipMemcpyAsync
+ * device-to-host on `stream` (plus one device-to-device copy into the
  * mirror).  Every transfer is checked before anything is issued: one with a
  * coordinate out of range makes the call return HISPARSE_EINVAL with nothing
  * enqueued.  On a HIP error the runs before the failing one stay enqueued.
