@@ -605,6 +605,9 @@ def main():
     walls = []
     for name in kinds:
         setattr(g.cache, name, timed(name, origs[name]))
+    # the detail run also keeps the kernel's per-request counters
+    # (hisparse_set_stats) over its timed steps, to cross-check the tiers
+    kstats = torch.zeros(wl.R, 6, dtype=torch.int64, device=dev)
     try:
         for i in range(args.runs + 1):
             detail = i == args.runs
@@ -616,6 +619,7 @@ def main():
             sink["timed"] = not detail
             if detail:
                 recording.update(per_step)
+                g.cache.set_stats(kstats)
             t0 = time.perf_counter()
             for k in range(args.warmup, total):
                 if not detail:
@@ -630,6 +634,8 @@ def main():
     finally:
         for name in kinds:
             setattr(g.cache, name, origs[name])
+        g.cache.set_stats(None)
+    kcount = kstats.sum(0).cpu().numpy()
     wall = float(np.median(walls))
 
     entries = sum(int(np.count_nonzero(v >= 0)) for k in range(args.warmup, total) for v in topk_all[k].values())
@@ -726,6 +732,14 @@ def main():
     traffic = None if cb is None else cb[0] + cb[1]
     tr_us = trace_mean_us(wl.name, args.steps, args.warmup, args.runs)
     step_s = wall / args.steps
+    tiers = tier_shares(wl, topk_all, range(args.warmup, total), misses,
+                        g.block_table_np if wl.page_size else None)
+    # the same split from the kernel's own counters (entries, resident, fast
+    # path, newest, hit, miss), counted in the detail run's timed steps
+    tiers_kernel = dict(zip(("entries", "resident", "fast_path", "newest", "hit", "miss"), map(int, kcount)))
+    tiers["kernel_counters"] = tiers_kernel
+    tiers["kernel_counters_agree"] = all(tiers_kernel[k] == tiers["entries"][k] for k in tiers["entries"]) and \
+        tiers_kernel["entries"] == entries
     rec = {
         "metric": "top-k rows resolved/s per decode step; miss-copy GB/s as % of host-link peak",
         "value": entries / wall,
@@ -786,8 +800,7 @@ def main():
         "all_steps": all_steps,
         "replay": kind_stats("replay", replay_rows),
         "backup": kind_stats("backup", backup_rows),
-        "tiers": tier_shares(wl, topk_all, range(args.warmup, total), misses,
-                             g.block_table_np if wl.page_size else None),
+        "tiers": tiers,
         "misses_per_step": misses / args.steps,
         "cpu_baseline": cpu,
     }

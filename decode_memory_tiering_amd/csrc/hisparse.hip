@@ -76,6 +76,14 @@ __device__ __forceinline__ int lanes_below(uint64_t mask)
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
+// Adds v, summed over the wave, to *dst: one device atomic per wave.
+__device__ __forceinline__ void wave_add_stat(unsigned long long* dst, int v)
+{
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0 && v) atomicAdd(dst, static_cast<unsigned long long>(v));
+}
+
 __device__ __forceinline__ uint32_t hash_slot(int32_t t, int bits)
 {
     return (static_cast<uint32_t>(t) * 0x9E3779B1u) >> (32 - bits);
@@ -273,6 +281,7 @@ struct SwapInArgs {
     int32_t paged, max_pages, page_size, hot_row_base;
     const uint8_t* new_rows;     // [nb][rb] or null: the forward's KV write fused into this launch
     uint8_t* backup_host;        // [R][max_seq][rb] or null: with new_rows, the eager backup fused in too
+    unsigned long long* stats;   // [R][HISPARSE_STAT_COUNT] or null: per-request counters, added to
 };
 
 constexpr unsigned long long kHashEmpty = ~0ull;
@@ -336,7 +345,9 @@ __device__ void fail_row(const SwapInArgs& a, int b, uint32_t flags)
 }
 
 // EB / EK: 64-entry chunks of the LRU list / top-k row held per wave.
-template <int EB, int EK>
+// STATS: the per-request counters of hisparse_set_stats are kept (a.stats
+// set); the instantiations without it are used otherwise and carry no cost.
+template <int EB, int EK, bool STATS>
 __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
 {
     extern __shared__ unsigned long long smem[];
@@ -376,8 +387,19 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
     // Tier 0 (resident request) and the short-sequence fast path: the slot
     // is the position; no state, no plan, no copy.
     if (!a.paged && ((a.resident && a.resident[b]) || L <= B)) {
-        for (int i = tid; i < K; i += nthr) out[i] = topk[i];
+        int valid = 0;
+        for (int i = tid; i < K; i += nthr) {
+            const int t = topk[i];
+            out[i] = t;
+            valid += t >= 0;
+        }
         if (tid == 0) a.plan_count[b] = 0;
+        const int rq = a.req_idx ? a.req_idx[b] : b;
+        if (STATS && rq >= 0 && rq < a.R) {
+            unsigned long long* st = a.stats + size_t(rq) * HISPARSE_STAT_COUNT;
+            wave_add_stat(st + HISPARSE_STAT_ENTRIES, valid);
+            wave_add_stat(st + ((a.resident && a.resident[b]) ? HISPARSE_STAT_RESIDENT : HISPARSE_STAT_FAST), valid);
+        }
         return;
     }
     const int r = a.req_idx ? a.req_idx[b] : b;
@@ -395,13 +417,22 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
             else if (t >= 0) (void)resident_row(bt_row, a.max_pages, a.page_size, t, &perr);
         }
         if (__syncthreads_or(perr != 0)) { fail_row(a, b, perr); return; }
+        int n_res = 0, n_fast = 0;
         for (int i = tid; i < K; i += nthr) {
             const int t = topk[i];
             uint32_t unused = 0;
             const int rr = t >= 0 ? resident_row(bt_row, a.max_pages, a.page_size, t, &unused) : -1;
             out[i] = t < 0 ? -1 : (rr >= 0 ? rr : hot_base + t);
+            n_res += rr >= 0;
+            n_fast += t >= 0 && rr < 0;
         }
         if (tid == 0) a.plan_count[b] = 0;
+        if (STATS) {
+            unsigned long long* st = a.stats + size_t(r) * HISPARSE_STAT_COUNT;
+            wave_add_stat(st + HISPARSE_STAT_ENTRIES, n_res + n_fast);
+            wave_add_stat(st + HISPARSE_STAT_RESIDENT, n_res);
+            wave_add_stat(st + HISPARSE_STAT_FAST, n_fast);
+        }
         return;
     }
     if (L > a.max_seq) { fail_row(a, b, HISPARSE_DERR_SEQ_LEN); return; }
@@ -667,6 +698,42 @@ __global__ __launch_bounds__(1024) void swap_in_kernel(SwapInArgs a)
 
     // -- miss copy: pinned host rows -> victim slots -----------------------
     copy.finish(tid);
+
+    // -- per-request counters (hisparse_set_stats) --------------------------
+    // After the copy, so the copy's registers are free: every valid entry
+    // is resident (paged tier 0, looked up again), the newest row (its out_s
+    // stayed B), a hit (one per hit slot) or a miss.  Wave counts come from
+    // ballots (wave-uniform); the LDS read here was written before the last
+    // barrier.
+    if (STATS) {
+        int n_res = 0, n_newest = 0;
+#pragma unroll
+        for (int k = 0; k < EK; ++k) {
+            const int c = k * nwaves + wave, i = c * kWave + lane;
+            const bool in = c < nck && i < K;
+            bool res = false;
+            if (in && a.paged) {
+                const int t = topk[i];
+                uint32_t unused = 0;
+                res = t >= 0 && resident_row(bt_row, a.max_pages, a.page_size, t, &unused) >= 0;
+            }
+            const bool nw = in && !res && s.out_s[i] == B;
+            n_res += __popcll(__ballot(res));
+            n_newest += __popcll(__ballot(nw));
+        }
+        unsigned long long* st = a.stats + size_t(r) * HISPARSE_STAT_COUNT;
+        if (lane == 0 && n_res + n_newest) {
+            atomicAdd(st + HISPARSE_STAT_RESIDENT, static_cast<unsigned long long>(n_res));
+            atomicAdd(st + HISPARSE_STAT_NEWEST, static_cast<unsigned long long>(n_newest));
+            atomicAdd(st + HISPARSE_STAT_ENTRIES, static_cast<unsigned long long>(n_res + n_newest));
+        }
+        if (tid == 0) {
+            const int hits = s.totals[0], misses = s.totals[1];
+            atomicAdd(st + HISPARSE_STAT_HIT, static_cast<unsigned long long>(hits));
+            atomicAdd(st + HISPARSE_STAT_MISS, static_cast<unsigned long long>(misses));
+            atomicAdd(st + HISPARSE_STAT_ENTRIES, static_cast<unsigned long long>(hits + misses));
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -933,24 +1000,24 @@ __global__ __launch_bounds__(256) void admit_fill_kernel(const uint8_t* host, ui
 typedef void (*SwapInFn)(SwapInArgs);
 
 template <int EB, int EK>
-SwapInFn pick2() { return &swap_in_kernel<EB, EK>; }
+SwapInFn pick2(bool stats) { return stats ? &swap_in_kernel<EB, EK, true> : &swap_in_kernel<EB, EK, false>; }
 
 template <int EB>
-SwapInFn pick_k(int ek)
+SwapInFn pick_k(int ek, bool stats)
 {
-    if (ek <= 1) return pick2<EB, 1>();
-    if (ek <= 2) return pick2<EB, 2>();
-    if (ek <= 4) return pick2<EB, 4>();
+    if (ek <= 1) return pick2<EB, 1>(stats);
+    if (ek <= 2) return pick2<EB, 2>(stats);
+    if (ek <= 4) return pick2<EB, 4>(stats);
     return nullptr;
 }
 
-SwapInFn pick_kernel(int eb, int ek)
+SwapInFn pick_kernel(int eb, int ek, bool stats)
 {
-    if (eb <= 1) return pick_k<1>(ek);
-    if (eb <= 2) return pick_k<2>(ek);
-    if (eb <= 4) return pick_k<4>(ek);
-    if (eb <= 8) return pick_k<8>(ek);
-    if (eb <= 16) return pick_k<16>(ek);
+    if (eb <= 1) return pick_k<1>(ek, stats);
+    if (eb <= 2) return pick_k<2>(ek, stats);
+    if (eb <= 4) return pick_k<4>(ek, stats);
+    if (eb <= 8) return pick_k<8>(ek, stats);
+    if (eb <= 16) return pick_k<16>(ek, stats);
     return nullptr;
 }
 
@@ -980,7 +1047,7 @@ struct hisparse_ctx {
     int32_t K = 0, B = 0, layers = 0, R = 0, max_seq = 0, rb = 0;
     int block = kDefaultBlock, replay_grid = kDefaultReplayGrid, hash_bits = 1;
     size_t lds = 0;
-    SwapInFn swap_in_fn = nullptr;
+    SwapInFn swap_in_fn[2] = {nullptr, nullptr};   // without / with the per-request counters
     // per layer (fixed arrays: a context holds no heap memory beyond itself)
     const uint8_t* host[kMaxLayers] = {};   // device-usable address of each layer's host pool
     uint8_t* host_ptr[kMaxLayers] = {};     // the same pool's host address (runtime-copy transfers)
@@ -989,6 +1056,7 @@ struct hisparse_ctx {
     int32_t* lru[kMaxLayers] = {};          // null for skip layers
     int32_t* tok[kMaxLayers] = {};
     uint32_t* err = nullptr;
+    unsigned long long* stats = nullptr;    // caller's per-request counters, or null (hisparse_set_stats)
     bool in_scratch = false;                // state lives in the static scratch array (hisparse_init_static)
 };
 
@@ -1159,8 +1227,9 @@ int init_common(const hisparse_config* cfg, hisparse_ctx* c)
     const int nwaves = block / kWave;
     const int eb = ((B + 63) / 64 + nwaves - 1) / nwaves;
     const int ek = ((K + 63) / 64 + nwaves - 1) / nwaves;
-    c->swap_in_fn = pick_kernel(eb, ek);
-    if (!c->swap_in_fn) return HISPARSE_EINVAL;
+    c->swap_in_fn[0] = pick_kernel(eb, ek, false);
+    c->swap_in_fn[1] = pick_kernel(eb, ek, true);
+    if (!c->swap_in_fn[0] || !c->swap_in_fn[1]) return HISPARSE_EINVAL;
     int max_lds = 0;
     if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device) != hipSuccess)
         return HISPARSE_EHIP(hipGetLastError());
@@ -1175,9 +1244,11 @@ int init_common(const hisparse_config* cfg, hisparse_ctx* c)
         if (e != hipSuccess) return HISPARSE_EHIP(e);
     }
     if (c->lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(c->swap_in_fn),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(c->lds));
-        if (e != hipSuccess) return HISPARSE_EHIP(e);
+        for (SwapInFn fn : c->swap_in_fn) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(c->lds));
+            if (e != hipSuccess) return HISPARSE_EHIP(e);
+        }
     }
     return HISPARSE_OK;
 }
@@ -1336,9 +1407,10 @@ int launch_swap_in(hisparse_ctx* c, int32_t anchor_layer, const int32_t* topk_id
     a.hot_row_base = hot_row_base;
     a.new_rows = static_cast<const uint8_t*>(new_rows);
     a.backup_host = backup ? const_cast<uint8_t*>(c->host[anchor_layer]) : nullptr;
+    a.stats = c->stats;
     void* args[] = {&a};
-    return hip_rc(hipLaunchKernel(reinterpret_cast<const void*>(c->swap_in_fn), dim3(nb), dim3(c->block), args,
-                                  c->lds, stream));
+    return hip_rc(hipLaunchKernel(reinterpret_cast<const void*>(c->swap_in_fn[c->stats ? 1 : 0]), dim3(nb),
+                                  dim3(c->block), args, c->lds, stream));
 }
 
 }  // namespace
@@ -1563,6 +1635,14 @@ int hisparse_set_state(hisparse_ctx* c, int32_t anchor_layer, const int32_t* lru
     hipError_t e = hipMemcpyAsync(c->lru[anchor_layer], lru, bytes, hipMemcpyDeviceToDevice, stream);
     if (e == hipSuccess) e = hipMemcpyAsync(c->tok[anchor_layer], slot_tok, bytes, hipMemcpyDeviceToDevice, stream);
     return hip_rc(e);
+}
+
+int hisparse_set_stats(hisparse_ctx* c, uint64_t* stats)
+{
+    if (!usable(c)) return HISPARSE_EINVAL;
+    if (stats && (reinterpret_cast<uintptr_t>(stats) & 7u)) return HISPARSE_EINVAL;
+    c->stats = reinterpret_cast<unsigned long long*>(stats);
+    return HISPARSE_OK;
 }
 
 int hisparse_get_error(hisparse_ctx* c, uint32_t* flags, int clear, hipStream_t stream)

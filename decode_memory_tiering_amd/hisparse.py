@@ -31,6 +31,10 @@ HISPARSE_DERR_STATE = 0x10
 HISPARSE_DERR_PLAN = 0x20
 HISPARSE_DERR_PAGE = 0x40
 
+HISPARSE_STAT_ENTRIES, HISPARSE_STAT_RESIDENT, HISPARSE_STAT_FAST = 0, 1, 2
+HISPARSE_STAT_NEWEST, HISPARSE_STAT_HIT, HISPARSE_STAT_MISS = 3, 4, 5
+HISPARSE_STAT_COUNT = 6
+
 HISPARSE_HOST_DEFAULT = 0
 HISPARSE_HOST_COHERENT = 1
 HISPARSE_HOST_NONCOHERENT = 2
@@ -43,7 +47,7 @@ EXPORTS = (
     "hisparse_store_swap_in_paged_backup",
     "hisparse_replay_plan", "hisparse_backup", "hisparse_spill", "hisparse_import", "hisparse_spill_dma",
     "hisparse_import_dma", "hisparse_get_state",
-    "hisparse_set_state", "hisparse_get_error", "hisparse_host_alloc", "hisparse_host_free",
+    "hisparse_set_state", "hisparse_set_stats", "hisparse_get_error", "hisparse_host_alloc", "hisparse_host_free",
     "hisparse_swap_in_lds_bytes", "hisparse_strerror", "hisparse_version",
 )
 
@@ -116,6 +120,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hisparse_import_dma.argtypes = [P, I32, P, I32, I32, P, I32, P, I32, P]
     lib.hisparse_get_state.argtypes = [P, I32, P, P, P]
     lib.hisparse_set_state.argtypes = [P, I32, P, P, P]
+    lib.hisparse_set_stats.argtypes = [P, P]
     lib.hisparse_get_error.argtypes = [P, ctypes.POINTER(U32), ctypes.c_int, P]
     lib.hisparse_host_alloc.argtypes = [ctypes.c_size_t, U32, ctypes.POINTER(ctypes.c_void_p)]
     lib.hisparse_host_free.argtypes = [P]
@@ -324,6 +329,11 @@ def hisparse_set_state(ctx: int, anchor_layer: int, lru, slot_tok, stream=None) 
            "hisparse_set_state")
 
 
+def hisparse_set_stats(ctx: int, stats) -> None:
+    """stats: device tensor [R][HISPARSE_STAT_COUNT] int64 (read as uint64), or None."""
+    _check(_lib().hisparse_set_stats(ctx, _ptr(stats)), "hisparse_set_stats")
+
+
 def hisparse_get_error(ctx: int, clear: bool = True, stream=None) -> int:
     v = ctypes.c_uint32()
     _check(_lib().hisparse_get_error(ctx, ctypes.byref(v), int(clear), _stream(stream)), "hisparse_get_error")
@@ -480,6 +490,9 @@ class HiSparseCache:
 
     def set_state(self, anchor, lru, tok, stream=None):
         hisparse_set_state(self.ctx, anchor, lru, tok, stream)
+
+    def set_stats(self, stats):
+        hisparse_set_stats(self.ctx, stats)
 
     def get_error(self, clear=True, stream=None) -> int:
         return hisparse_get_error(self.ctx, clear, stream)

@@ -94,6 +94,16 @@ extern "C" {
 #define HISPARSE_DERR_PAGE       0x40u /* paged: block-table entry < -1, or a physical row beyond INT32_MAX;
                                           spill / import: a transfer coordinate out of range */
 
+/* Per-request counters (hisparse_set_stats), one row of HISPARSE_STAT_COUNT
+ * uint64 per request. */
+#define HISPARSE_STAT_ENTRIES  0   /* valid top-k entries resolved (not -1)              */
+#define HISPARSE_STAT_RESIDENT 1   /* resolved in tier 0: resident request or page      */
+#define HISPARSE_STAT_FAST     2   /* resolved by the L <= B fast path (slot = position) */
+#define HISPARSE_STAT_NEWEST   3   /* the newest token's own row                          */
+#define HISPARSE_STAT_HIT      4   /* held in a hot slot                                  */
+#define HISPARSE_STAT_MISS     5   /* copied from the host pool (the plan count)          */
+#define HISPARSE_STAT_COUNT    6
+
 /* hisparse_host_alloc flags */
 #define HISPARSE_HOST_DEFAULT     0u   /* HIP's default pinned, mapped allocation */
 #define HISPARSE_HOST_COHERENT    1u   /* fine-grained: GPU accesses bypass its caches */
@@ -353,6 +363,20 @@ int hisparse_get_state(hisparse_ctx* ctx, int32_t anchor_layer, int32_t* lru,
                        int32_t* slot_tok, hipStream_t stream);
 int hisparse_set_state(hisparse_ctx* ctx, int32_t anchor_layer, const int32_t* lru,
                        const int32_t* slot_tok, hipStream_t stream);
+
+/* Count what the resolver serves, per request, without any readback on the
+ * hot path (hit rates are what the [HiCache] page reports for its tiers).
+ * stats: device memory, [R][HISPARSE_STAT_COUNT] uint64, 8-byte aligned,
+ * caller-owned and valid while set; NULL stops counting.  Every later launch
+ * of a swap-in call (all forms) adds each batch row's counts to row req_idx[b]
+ * with device atomics: its valid entries, split into resident, fast path,
+ * newest row, hits and misses (these five sum to the entries).  A batch row
+ * that fails its device-side checks adds nothing.  The library never reads or
+ * clears the buffer: the caller zeroes it and reads it when it likes, ordered
+ * after the launches it wants counted.  Host-only (stores the pointer); a
+ * launch captured in a HIP graph keeps the pointer set at capture.  Not
+ * defined by the pages (library infrastructure). */
+int hisparse_set_stats(hisparse_ctx* ctx, uint64_t* stats);
 
 /* Read (and optionally clear) the device error word.  Synchronizes the
  * stream: a diagnostic, never part of a decode step.  Not defined by the

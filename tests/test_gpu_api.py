@@ -235,6 +235,45 @@ def test_graph_capture_and_replay(form):
     c.close()
 
 
+def test_graph_capture_of_runtime_copy_transfers():
+    """hisparse_spill_dma and hisparse_import_dma captured once in a HIP graph
+    (their host-side transfer lists are read at capture), replayed with new
+    page contents copied into the captured source buffers (eager work and
+    synchronisation between replays); every replay must equal the oracle."""
+    R, B, K, rb, P = 4, 64, 24, 48, 16
+    max_seq = 200
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
+    o = _oracle_for(c)
+    rng = np.random.default_rng(9)
+    spill = np.array([(3, 0, 0, -1), (7, 1, 12, -1), (4, 1, 2, -1), (5, 1, 3, -1), (6, 1, 4, -1)], np.int32)
+    imp = np.array([(0, 0, 3, 4), (1, 0, 4, 5), (9, 2, 12, -1), (2, 3, 0, -1)], np.int32)
+    res_d = torch.zeros(20 * P, rb, dtype=torch.uint8, device="cuda")
+    stg_d = torch.zeros(10 * P, rb, dtype=torch.uint8, device="cuda")
+    mirror_d = torch.zeros(20 * P, rb, dtype=torch.uint8, device="cuda")
+    mirror_np = np.zeros((20 * P, rb), np.uint8)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            c.spill_dma(0, res_d, P, spill, s)
+            c.import_pages_dma(0, stg_d, P, mirror_d, imp, s)
+    torch.cuda.synchronize()
+    for step in range(5):
+        res = rng.integers(0, 256, size=(20 * P, rb), dtype=np.uint8)
+        stg = rng.integers(0, 256, size=(10 * P, rb), dtype=np.uint8)
+        res_d.copy_(_dev(res, torch.uint8))
+        stg_d.copy_(_dev(stg, torch.uint8))
+        g.replay()
+        _ = (mirror_d.sum() + 1).item()       # eager work + sync between replays
+        o.page_copy(0, P, res, spill)
+        o.page_copy(0, P, stg, imp, mirror=mirror_np)
+        assert np.array_equal(c.host_np[0], o.host[0]), f"replay {step}"
+        assert np.array_equal(mirror_d.cpu().numpy(), mirror_np), f"replay {step}"
+    assert c.get_error() == 0
+    c.close()
+
+
 def test_readmission_keeps_results_byte_correct():
     """Resetting a request's state mid-run (admit again) changes slot ids but
     never the bytes a slot resolves to: the host pool stays complete because
@@ -755,3 +794,68 @@ def test_paged_fused_request_subsets_via_req_idx():
     assert np.array_equal(c.host_np[0], o.host[0])
     assert c.get_error() == 0
     c.close()
+
+
+STATS_CASES = [
+    W.Workload("stats_mix", 3, (0, 0, 2), R=7, B=300, K=100, rb=32, steps=6, spec=2, n_resident=2,
+               seq_first=("uniform", 100, 900), seed=61),
+    W.Workload("stats_paged", 1, (0,), R=5, B=256, K=80, rb=32, steps=6, page_size=16, resident_page_frac=0.4,
+               seq_first=("uniform", 100, 1500), seed=62),
+]
+
+
+@pytest.mark.parametrize("wl", STATS_CASES, ids=lambda w: w.name)
+def test_per_request_counters_match_the_oracle(wl):
+    """hisparse_set_stats: over a multi-step decode (verify rows, skip layers,
+    resident requests or pages, fast path and slow rows), every request's
+    counters equal what the oracle's outputs and plan rows say: each valid
+    entry once, split into resident, fast path, newest row, hits and misses."""
+    from decode_memory_tiering_amd.runner import GpuRun, draw_topk, new_kv_all_layers
+    from oracle.runner import OracleRun
+    g = GpuRun(wl)
+    o = OracleRun(wl, host_pools=g.cache.host_np)
+    stats = torch.zeros(wl.R, H.HISPARSE_STAT_COUNT, dtype=torch.int64, device="cuda")
+    g.cache.set_stats(stats)
+    exp = np.zeros((wl.R, H.HISPARSE_STAT_COUNT), np.int64)
+    streams = {a: W.TopkStream(wl, a) for a in wl.anchors}
+    res = W.resident_mask(wl).astype(bool)
+    paged = wl.page_size > 0
+    for k in range(wl.steps):
+        topk = draw_topk(wl, streams, k)
+        nk = new_kv_all_layers(wl, k, "cuda")
+        L = W.seq_lens_at(wl, k)
+        g.step({a: _dev(v) for a, v in topk.items()}, nk, g.seq_lens(k), seq_lens_np=L)
+        outs, plans = o.step(k, topk, nk.cpu().numpy())
+        for a in wl.anchors:
+            for s in range(wl.spec):
+                x, out, cnt = topk[a][s], outs[a][s], plans[a][s].count
+                for r in range(wl.R):
+                    valid = x[r] >= 0
+                    nv = int(valid.sum())
+                    exp[r, H.HISPARSE_STAT_ENTRIES] += nv
+                    if not paged and res[r]:
+                        exp[r, H.HISPARSE_STAT_RESIDENT] += nv
+                        continue
+                    resid = valid & (out[r] >= 0) & (out[r] < o.hot_row_base) if paged else np.zeros_like(valid)
+                    nres = int(resid.sum())
+                    exp[r, H.HISPARSE_STAT_RESIDENT] += nres
+                    if L[r] <= wl.B:
+                        exp[r, H.HISPARSE_STAT_FAST] += nv - nres
+                        continue
+                    nnew = int((valid & ~resid & (x[r] == L[r] - 1)).sum())
+                    exp[r, H.HISPARSE_STAT_NEWEST] += nnew
+                    exp[r, H.HISPARSE_STAT_MISS] += int(cnt[r])
+                    exp[r, H.HISPARSE_STAT_HIT] += nv - nres - nnew - int(cnt[r])
+    torch.cuda.synchronize()
+    got = stats.cpu().numpy()
+    assert np.array_equal(got, exp), (got, exp)
+    assert (exp[:, H.HISPARSE_STAT_HIT] > 0).any() and (exp[:, H.HISPARSE_STAT_MISS] > 0).any()
+    g.cache.set_stats(None)                   # counting off: later launches add nothing
+    before = stats.clone()
+    g.readmit()
+    g.step({a: _dev(v) for a, v in draw_topk(wl, {a: W.TopkStream(wl, a) for a in wl.anchors}, 0).items()},
+           new_kv_all_layers(wl, 0, "cuda"), g.seq_lens(0), seq_lens_np=W.seq_lens_at(wl, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(stats, before)
+    assert g.cache.get_error() == 0
+    g.close()

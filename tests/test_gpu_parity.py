@@ -210,6 +210,23 @@ def test_buffer_above_8192_slots():
     _lockstep(wl)
 
 
+def test_million_token_context():
+    # production inputs reach 1M tokens (HiCache page): positions past 2^20
+    # through the hash, the slot map and the host-pool addressing
+    wl = W.Workload("million", 1, (0,), R=2, B=2048, K=512, rb=16, steps=4, topk_kind="uniform",
+                    seq_first=("list", 1_000_000, 1_048_600), seed=44)
+    st = _lockstep(wl)
+    assert st["misses"] > 0
+
+
+def test_wide_rows():
+    # 8 KB per token (512 chunks of 16 bytes per row): the copy's (row, column)
+    # walk across many columns, rows much wider than a wave's 1 KB of loads
+    wl = W.Workload("wide_rows", 2, (0, 0), R=3, B=300, K=100, rb=8192, steps=5,
+                    seq_first=("list", 250, 900, 3000), seed=45)
+    _lockstep(wl)
+
+
 def test_maximum_sizes():
     # the largest buffer and top-k the library accepts: 16384 slots, 4096 top-k entries
     wl = W.Workload("max", 1, (0,), R=2, B=16384, K=4096, rb=16, steps=4,
