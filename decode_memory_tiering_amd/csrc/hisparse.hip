@@ -18,9 +18,16 @@
 //                    guide, "Decode Workflow" (eager backup).
 //   page_copy_kernel whole pages: resident -> host (spill), staging -> host
 //                    with an optional resident mirror (import).  vLLM design
-//                    note, "Spill transaction" and "P/D import target".
-//   store_newest_kernel, admit_*_kernel, init_state_kernel: the forward's KV
-//                    write, request admission, context set-up.
+//                    note, "Spill transaction" and "P/D import target".  The
+//                    same transfers also go as runtime copies from a host-side
+//                    list (hisparse_spill_dma / hisparse_import_dma).
+//   store_newest_kernel, admit_*_kernel, init_state_kernel, clear_word_kernel:
+//                    the forward's KV write, request admission, context
+//                    set-up.
+// Host side: the C ABI of include/hisparse.h, with contexts either on memory
+// from hipMalloc (hisparse_init) or in a static per-device scratch array
+// (hisparse_init_static), and optional per-request counters that the
+// swap-in launches add to (hisparse_set_stats).
 //
 // Tie-breaks the pages leave open (same readings as the oracle, reached
 // independently here): victims come from the least-recent end of the LRU list
