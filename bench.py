@@ -208,7 +208,7 @@ def tier_shares(wl, topk_all, steps, misses, block_table=None):
 
 
 def cpu_baseline(wl, steps, warmup, host_pools, topk_all, newkv_all, budget_s=10.0, max_threads=16,
-                 pool_steps=None):
+                 pool_steps=None, rows_per_rep=None):
     """The oracle, as it stands, on the same inputs and the same timed steps
     as the GPU (steps [warmup, steps) of the decode, the warm-up steps run
     untimed), driven from C (oracle/oracle_timing.c: no Python inside the
@@ -241,9 +241,15 @@ def cpu_baseline(wl, steps, warmup, host_pools, topk_all, newkv_all, budget_s=10
     tn, repsn = sweep(threads) if threads > 1 else (t1, reps1)
     what = (f"steps {warmup}..{steps - 1} of the same decode as the GPU run (warm-up steps untimed), all "
             f"{wl.R} requests and {wl.num_layers} layer(s), re-admitted before each repetition")
+    # rows_per_rep: the rows a repetition copies (misses and replayed rows of
+    # the timed steps, the same as the GPU's); the oracle copies them from the
+    # pinned pool into its host mirror of the hot buffer
+    copy = (lambda reps, t: rows_per_rep * wl.rb * reps / t / 1e9) if rows_per_rep is not None else None
     return dict(value=per_rep * reps1 / t1, unit="top-k entries resolved/s", cores=1, kind="oracle",
+                copy_gbps=copy(reps1, t1) if copy else None,
                 sample=f"{reps1} repetition(s) of {what}; single thread, timed oracle work {t1:.2f}s",
                 threads=dict(value=per_rep * repsn / tn, cores=threads,
+                             copy_gbps=copy(repsn, tn) if copy else None,
                              sample=f"{repsn} repetition(s), requests split into {threads} shares on "
                                     f"{threads} threads, timed wall {tn:.2f}s"))
 
@@ -724,7 +730,8 @@ def main():
     if not args.no_cpu_baseline:
         newkv_np = [t.cpu().numpy() for t in newkv_dev[:total]]
         g.close()
-        cpu = cpu_baseline(wl, total, args.warmup, host_copy, topk_all, newkv_np, pool_steps=n_gen)
+        cpu = cpu_baseline(wl, total, args.warmup, host_copy, topk_all, newkv_np, pool_steps=n_gen,
+                           rows_per_rep=misses + replay_rows)
     else:
         g.close()
 

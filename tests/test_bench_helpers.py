@@ -80,3 +80,30 @@ def test_algorithmic_bytes_split():
     entries = sum(int((v >= 0).sum()) for t in topk_all for v in t.values())
     assert alg["entries"] == entries
     assert alg["hbm_read"] == entries * 4 + alg["slow_rows"] * 8 * wl.B + 4 * wl.rb
+
+
+def test_cpu_baseline_reports_entries_and_copy_rate():
+    # the benchmark's CPU-baseline leg on a small decode: the oracle timed
+    # from C over the timed steps, on one thread and on request shares;
+    # entries/s and copy GB/s come from the same repetitions, so their ratio
+    # is the rows copied per entry resolved
+    wl = CASES[0]
+    steps, warmup = wl.steps, 2
+    streams = {a: W.TopkStream(wl, a) for a in wl.anchors}
+    topk_all = [draw_topk(wl, streams, k) for k in range(steps)]
+    newkv = [new_kv_all_layers(wl, k, "cpu").numpy() for k in range(steps)]
+    o = OracleRun(wl, steps)
+    rows = 0
+    for k in range(steps):
+        _, plans = o.step(k, topk_all[k], newkv[k])
+        if k >= warmup:   # misses, and every skip layer's replay of its anchor's plans
+            rows += sum(int(p.count.sum()) for a in wl.anchors for p in plans[a])
+            rows += sum(int(p.count.sum()) for x in wl.skip_layers for p in plans[wl.anchor_of[x]])
+    pools = [np.array(h, copy=True) for h in OracleRun(wl, steps).orc.host]
+    got = bench.cpu_baseline(wl, steps, warmup, pools, topk_all, newkv, budget_s=0.05, max_threads=2,
+                             rows_per_rep=rows)
+    entries = sum(int((v >= 0).sum()) for t in topk_all[warmup:] for v in t.values())
+    assert got["kind"] == "oracle" and got["cores"] == 1 and got["value"] > 0
+    assert got["threads"]["cores"] == min(2, len(__import__("os").sched_getaffinity(0)))
+    assert got["copy_gbps"] == pytest.approx(got["value"] / entries * rows * wl.rb / 1e9)
+    assert got["threads"]["copy_gbps"] == pytest.approx(got["threads"]["value"] / entries * rows * wl.rb / 1e9)
