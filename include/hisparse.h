@@ -155,8 +155,8 @@ int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out);
  * carved from one static array of the library, hisparse_static_scratch_bytes()
  * = 32 MiB, which each device the library runs on holds until the process
  * ends; the context object is a static slot of that device.  The state needs
- * 256 + 2 * ceil256(R * B * 4) bytes per anchor layer; a configuration that
- * does not fit returns HISPARSE_ENOSPC.  One such context per device at a
+ * 256 bytes plus 2 * ceil256(R * B * 4) bytes per anchor layer; a
+ * configuration that does not fit returns HISPARSE_ENOSPC.  One such context per device at a
  * time: while one is live (until hisparse_destroy), another call on that
  * device returns HISPARSE_EBUSY.  The array keeps the previous context's
  * contents, so this call writes every byte the new context uses (state as
