@@ -796,23 +796,30 @@ def test_paged_fused_request_subsets_via_req_idx():
     c.close()
 
 
+_STATS_MIX = W.Workload("stats_mix", 3, (0, 0, 2), R=7, B=300, K=100, rb=32, steps=6, spec=2, n_resident=2,
+                        seq_first=("uniform", 100, 900), seed=61)
+# (workload, workgroup size): the counting instantiations of 1, 4 and 16
+# chunks per wave; the widest (16 buffer chunks, 4 top-k chunks per wave) is
+# the one whose counting spills registers
 STATS_CASES = [
-    W.Workload("stats_mix", 3, (0, 0, 2), R=7, B=300, K=100, rb=32, steps=6, spec=2, n_resident=2,
-               seq_first=("uniform", 100, 900), seed=61),
-    W.Workload("stats_paged", 1, (0,), R=5, B=256, K=80, rb=32, steps=6, page_size=16, resident_page_frac=0.4,
-               seq_first=("uniform", 100, 1500), seed=62),
+    (_STATS_MIX, 1024),
+    (_STATS_MIX, 128),
+    (W.Workload("stats_paged", 1, (0,), R=5, B=256, K=80, rb=32, steps=6, page_size=16, resident_page_frac=0.4,
+                seq_first=("uniform", 100, 1500), seed=62), 1024),
+    (W.Workload("stats_widest", 2, (0, 1), R=4, B=16384, K=4096, rb=16, steps=4, n_resident=1,
+                seq_first=("list", 40000, 12000, 20000, 30000), seed=63), 1024),   # resident: the 30000 one
 ]
 
 
-@pytest.mark.parametrize("wl", STATS_CASES, ids=lambda w: w.name)
-def test_per_request_counters_match_the_oracle(wl):
+@pytest.mark.parametrize("wl,block", STATS_CASES, ids=lambda c: getattr(c, "name", str(c)))
+def test_per_request_counters_match_the_oracle(wl, block):
     """hisparse_set_stats: over a multi-step decode (verify rows, skip layers,
     resident requests or pages, fast path and slow rows), every request's
     counters equal what the oracle's outputs and plan rows say: each valid
     entry once, split into resident, fast path, newest row, hits and misses."""
     from decode_memory_tiering_amd.runner import GpuRun, draw_topk, new_kv_all_layers
     from oracle.runner import OracleRun
-    g = GpuRun(wl)
+    g = GpuRun(wl, block_size=block)
     o = OracleRun(wl, host_pools=g.cache.host_np)
     stats = torch.zeros(wl.R, H.HISPARSE_STAT_COUNT, dtype=torch.int64, device="cuda")
     g.cache.set_stats(stats)

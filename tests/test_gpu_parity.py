@@ -210,6 +210,15 @@ def test_buffer_above_8192_slots():
     _lockstep(wl)
 
 
+def test_large_buffer_with_the_standard_top_k():
+    # a buffer above 8192 slots with top_k 2048: the instantiation with 16
+    # buffer chunks and 2 top-k chunks per wave
+    wl = W.Workload("wide_k2048", 1, (0,), R=2, B=12288, K=2048, rb=16, steps=4,
+                    seq_first=("list", 20000, 30000), seed=46)
+    st = _lockstep(wl)
+    assert st["misses"] > 0
+
+
 def test_million_token_context():
     # production inputs reach 1M tokens (HiCache page): positions past 2^20
     # through the hash, the slot map and the host-pool addressing
