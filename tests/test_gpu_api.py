@@ -43,9 +43,10 @@ def _dev(a, dtype=torch.int32):
 @pytest.mark.parametrize("form", ["separate", "fused"])
 def test_request_subsets_via_req_idx(form):
     """Each step only some requests decode, in a shuffled batch order (three
-    launches, or the one fused launch)."""
+    launches, or the one fused launch); a skip layer replays the anchor's plan
+    for the same batch rows, through the same mapping."""
     R, B, K, rb, max_seq = 10, 64, 24, 32, 600
-    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq, layers=2, anchor_of=(0, 0))
     o = _oracle_for(c)
     rng = np.random.default_rng(1)
     L = rng.integers(30, 300, size=R).astype(np.int32)          # current length per request
@@ -68,17 +69,25 @@ def test_request_subsets_via_req_idx(form):
             c.store_newest(0, _dev(new, torch.uint8), _dev(Lb), None, _dev(idx))
             c.swap_in(0, _dev(topk), _dev(Lb), None, _dev(idx), out, plan)
             c.backup(0, _dev(Lb), None, _dev(idx))
+        new1 = rng.integers(0, 256, size=(nb, rb), dtype=np.uint8)
+        c.store_newest(1, _dev(new1, torch.uint8), _dev(Lb), None, _dev(idx))
+        c.replay_plan(1, plan, _dev(idx))
+        c.backup(1, _dev(Lb), None, _dev(idx))
         o.store_newest(0, new, Lb, None, idx)
         eo, ep = o.swap_in(0, topk, Lb, None, idx)
         o.backup(0, Lb, None, idx)
+        o.store_newest(1, new1, Lb, None, idx)
+        o.replay(1, ep, idx)
+        o.backup(1, Lb, None, idx)
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eo)
         assert np.array_equal(plan.count.cpu().numpy(), ep.count)
         lru, tok = c.get_state(0)
         assert np.array_equal(lru.cpu().numpy(), o.lru[0]) and np.array_equal(tok.cpu().numpy(), o.tok[0])
         L[idx] += 1
-    assert np.array_equal(c.hot[0].cpu().numpy(), o.hot[0])
-    assert np.array_equal(c.host_np[0], o.host[0])
+    for l in range(2):
+        assert np.array_equal(c.hot[l].cpu().numpy(), o.hot[l])
+        assert np.array_equal(c.host_np[l], o.host[l])
     assert c.get_error() == 0
     c.close()
 
