@@ -40,11 +40,14 @@ def _dev(a, dtype=torch.int32):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype)
 
 
+@pytest.mark.parametrize("resident", [False, True], ids=["no_resident", "resident"])
 @pytest.mark.parametrize("form", ["separate", "fused"])
-def test_request_subsets_via_req_idx(form):
+def test_request_subsets_via_req_idx(form, resident):
     """Each step only some requests decode, in a shuffled batch order (three
     launches, or the one fused launch); a skip layer replays the anchor's plan
-    for the same batch rows, through the same mapping."""
+    for the same batch rows, through the same mapping.  With `resident`, a
+    random quarter of the batch rows is marked resident each step (the mask
+    is per batch row, like the rest of the batch's inputs)."""
     R, B, K, rb, max_seq = 10, 64, 24, 32, 600
     c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq, layers=2, anchor_of=(0, 0))
     o = _oracle_for(c)
@@ -61,24 +64,26 @@ def test_request_subsets_via_req_idx(form):
                          np.concatenate([rng.permutation(int(x)), -np.ones(K - int(x), np.int64)])
                          for x in Lb]).astype(np.int32)
         new = rng.integers(0, 256, size=(nb, rb), dtype=np.uint8)
+        res = (rng.random(nb) < 0.25).astype(np.uint8) if resident else None
+        rd = None if res is None else _dev(res, torch.uint8)
         out = torch.empty(nb, K, dtype=torch.int32, device="cuda")
         plan = H.Plan.empty(nb, K)
         if form == "fused":
-            c.store_swap_in_backup(0, _dev(new, torch.uint8), _dev(topk), _dev(Lb), None, _dev(idx), out, plan)
+            c.store_swap_in_backup(0, _dev(new, torch.uint8), _dev(topk), _dev(Lb), rd, _dev(idx), out, plan)
         else:
-            c.store_newest(0, _dev(new, torch.uint8), _dev(Lb), None, _dev(idx))
-            c.swap_in(0, _dev(topk), _dev(Lb), None, _dev(idx), out, plan)
-            c.backup(0, _dev(Lb), None, _dev(idx))
+            c.store_newest(0, _dev(new, torch.uint8), _dev(Lb), rd, _dev(idx))
+            c.swap_in(0, _dev(topk), _dev(Lb), rd, _dev(idx), out, plan)
+            c.backup(0, _dev(Lb), rd, _dev(idx))
         new1 = rng.integers(0, 256, size=(nb, rb), dtype=np.uint8)
-        c.store_newest(1, _dev(new1, torch.uint8), _dev(Lb), None, _dev(idx))
+        c.store_newest(1, _dev(new1, torch.uint8), _dev(Lb), rd, _dev(idx))
         c.replay_plan(1, plan, _dev(idx))
-        c.backup(1, _dev(Lb), None, _dev(idx))
-        o.store_newest(0, new, Lb, None, idx)
-        eo, ep = o.swap_in(0, topk, Lb, None, idx)
-        o.backup(0, Lb, None, idx)
-        o.store_newest(1, new1, Lb, None, idx)
+        c.backup(1, _dev(Lb), rd, _dev(idx))
+        o.store_newest(0, new, Lb, res, idx)
+        eo, ep = o.swap_in(0, topk, Lb, res, idx)
+        o.backup(0, Lb, res, idx)
+        o.store_newest(1, new1, Lb, res, idx)
         o.replay(1, ep, idx)
-        o.backup(1, Lb, None, idx)
+        o.backup(1, Lb, res, idx)
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eo)
         assert np.array_equal(plan.count.cpu().numpy(), ep.count)
