@@ -219,6 +219,16 @@ def test_large_buffer_with_the_standard_top_k():
     assert st["misses"] > 0
 
 
+@pytest.mark.parametrize("prefetch", [True, False], ids=["prefetch", "inline"])
+def test_batch_wider_than_the_replay_workgroup(prefetch):
+    # 600 batch rows: the replay's prefix of the plan counts runs over several
+    # rows per thread (256 threads), and the swap-in grid has 600 workgroups
+    wl = W.Workload("wide_batch", 3, (0, 0, 0), R=600, B=64, K=24, rb=16, steps=4, spec=2,
+                    seq_first=("uniform", 30, 300), seed=47)
+    st = _lockstep(wl, prefetch=prefetch)
+    assert st["misses"] > 0
+
+
 def test_million_token_context():
     # production inputs reach 1M tokens (HiCache page): positions past 2^20
     # through the hash, the slot map and the host-pool addressing
