@@ -89,7 +89,12 @@ extern "C" {
 #define HISPARSE_DERR_TOPK_DUP   0x2u  /* repeated position in a top-k row */
 #define HISPARSE_DERR_SEQ_LEN    0x4u  /* L < 1, or L > max_seq_len where the host pool is addressed */
 #define HISPARSE_DERR_REQ_IDX    0x8u  /* req_idx[b] outside [0, R) */
-#define HISPARSE_DERR_STATE      0x10u /* lru not a permutation / slot map not injective or out of range */
+#define HISPARSE_DERR_STATE      0x10u /* corrupt LRU state, as far as a swap-in can see it: an lru
+                                          entry outside [0, B), a slot-map position outside
+                                          [-1, max_seq_len), two slots holding one position the row
+                                          asks for, or repeated lru entries that leave fewer non-hit
+                                          slots than misses.  The library never produces such state;
+                                          only hisparse_set_state can bring it in, unchecked. */
 #define HISPARSE_DERR_PLAN       0x20u /* replay: count > K, or a (pos, slot) pair out of range */
 #define HISPARSE_DERR_PAGE       0x40u /* paged: block-table entry < -1, or a physical row beyond INT32_MAX;
                                           spill / import: a transfer coordinate out of range */
@@ -358,7 +363,12 @@ int hisparse_import_dma(hisparse_ctx* ctx, int32_t layer, const void* staging, i
 
 /* Copy an anchor layer's state out of / into the library ([R][B] int32 each,
  * device pointers).  For tests and checkpointing; asynchronous on stream.
- * Not defined by the pages (library infrastructure). */
+ * set_state does not check what it copies in: each lru row must be a
+ * permutation of 0..B-1 and each slot map hold distinct positions or -1, as
+ * get_state returns them.  A swap-in flags the corruptions it can see
+ * (HISPARSE_DERR_STATE) and fails that row; others (say, an lru row that
+ * repeats a slot no entry hits) give wrong slot ids but never an access out
+ * of bounds.  Not defined by the pages (library infrastructure). */
 int hisparse_get_state(hisparse_ctx* ctx, int32_t anchor_layer, int32_t* lru,
                        int32_t* slot_tok, hipStream_t stream);
 int hisparse_set_state(hisparse_ctx* ctx, int32_t anchor_layer, const int32_t* lru,
