@@ -970,11 +970,12 @@ __global__ __launch_bounds__(64) void clear_word_kernel(uint32_t* w)
 }
 
 __global__ __launch_bounds__(256) void admit_state_kernel(int32_t* lru, int32_t* tok, const int32_t* req_ids,
-                                                          const int32_t* L0s, int R, int B, uint32_t* err)
+                                                          const int32_t* L0s, int R, int B, int max_seq,
+                                                          uint32_t* err)
 {
     const int r = req_ids[blockIdx.x];
     const int L0 = L0s[blockIdx.x];
-    if (r < 0 || r >= R || L0 < 0) {
+    if (r < 0 || r >= R || L0 < 0 || L0 > max_seq) {   // admit_fill_kernel skips the same entries
         if (threadIdx.x == 0) atomicOr(err, (r < 0 || r >= R) ? HISPARSE_DERR_REQ_IDX : HISPARSE_DERR_SEQ_LEN);
         return;
     }
@@ -1009,12 +1010,17 @@ typedef void (*SwapInFn)(SwapInArgs);
 template <int EB, int EK>
 SwapInFn pick2(bool stats) { return stats ? &swap_in_kernel<EB, EK, true> : &swap_in_kernel<EB, EK, false>; }
 
+// K <= B gives EK <= EB, so only those instantiations exist.
 template <int EB>
 SwapInFn pick_k(int ek, bool stats)
 {
     if (ek <= 1) return pick2<EB, 1>(stats);
-    if (ek <= 2) return pick2<EB, 2>(stats);
-    if (ek <= 4) return pick2<EB, 4>(stats);
+    if constexpr (EB >= 2) {
+        if (ek <= 2) return pick2<EB, 2>(stats);
+    }
+    if constexpr (EB >= 4) {
+        if (ek <= 4) return pick2<EB, 4>(stats);
+    }
     return nullptr;
 }
 
@@ -1369,7 +1375,7 @@ int hisparse_admit(hisparse_ctx* c, int32_t anchor_layer, const int32_t* req_ids
     if (n == 0) return HISPARSE_OK;
     if (!req_ids || !seq_len0) return HISPARSE_EINVAL;
     hipLaunchKernelGGL(admit_state_kernel, dim3(n), dim3(256), 0, stream, c->lru[anchor_layer],
-                       c->tok[anchor_layer], req_ids, seq_len0, c->R, c->B, c->err);
+                       c->tok[anchor_layer], req_ids, seq_len0, c->R, c->B, c->max_seq, c->err);
     for (int l = 0; l < c->layers; ++l) {
         if (c->anchor_of[l] != anchor_layer) continue;
         hipLaunchKernelGGL(admit_fill_kernel, dim3(n, 64), dim3(256), 0, stream, c->host[l], c->hot[l],

@@ -183,11 +183,10 @@ void hisparse_destroy(hisparse_ctx* ctx);
  * arrays): the anchor layer's state is reset (lru = 0..B-1; slot map =
  * identity if L0 <= B, else empty), and when L0 <= B the rows [0, L0) of
  * every layer sharing this anchor are copied from the host pool into the hot
- * buffer at slot = position.  An entry with r outside [0, R) or L0 < 0 is
- * skipped and sets HISPARSE_DERR_REQ_IDX or HISPARSE_DERR_SEQ_LEN; L0 must
- * not exceed max_seq_len, which is not checked (with max_seq_len < L0 <= B
- * the rows are not copied and the fast path would serve stale rows).
- * [SGL] "Decode Workflow" (fast path: every KV row already in the buffer). */
+ * buffer at slot = position.  An entry with r outside [0, R), L0 < 0 or
+ * L0 > max_seq_len is skipped (state and rows untouched) and sets
+ * HISPARSE_DERR_REQ_IDX or HISPARSE_DERR_SEQ_LEN.  [SGL] "Decode Workflow"
+ * (fast path: every KV row already in the buffer). */
 int hisparse_admit(hisparse_ctx* ctx, int32_t anchor_layer, const int32_t* req_ids,
                    const int32_t* seq_len0, int32_t n, hipStream_t stream);
 

@@ -144,6 +144,8 @@ class Oracle:
         req_ids = _i32(req_ids)
         seq_len0 = _i32(seq_len0)
         for r, L0 in zip(req_ids.tolist(), seq_len0.tolist()):
+            if L0 > self.max_seq:    # the prefill's rows must lie in the host pool
+                raise OracleError(ORC_EPRECOND, "admit: prompt longer than the host pool")
             lru = np.empty(self.B, np.int32)
             tok = np.empty(self.B, np.int32)
             self._check(self.lib.orc_admit_state(self.B, L0, _ptr(lru), _ptr(tok)), "admit_state")

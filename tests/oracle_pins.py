@@ -364,6 +364,11 @@ def pin_preconditions(lib) -> List[str]:
         fails.append("precondition: non-injective slot map accepted")
     except OracleError:
         pass
+    try:
+        orc.admit(0, [0], [41])
+        fails.append("precondition: a prompt longer than the host pool admitted")
+    except OracleError:
+        pass
     return fails
 
 

@@ -163,6 +163,26 @@ def test_bad_rows_fail_alone(case, flag):
     c.close()
 
 
+def test_admission_checks_each_entry():
+    """An admission entry with a request index out of range, a negative
+    prompt length or a prompt longer than the host pool is skipped with its
+    error bit; the other entries are admitted."""
+    c = _cache(R=4, B=64, max_seq=400)
+    lru0, tok0 = c.get_state(0)
+    c.admit(0, _dev(np.array([0, 1, 7, 2], np.int32)), _dev(np.array([30, 401, 20, -1], np.int32)))
+    torch.cuda.synchronize()
+    flags = c.get_error()
+    assert flags & H.HISPARSE_DERR_SEQ_LEN and flags & H.HISPARSE_DERR_REQ_IDX
+    lru, tok = c.get_state(0)
+    ident = torch.arange(64, dtype=torch.int32, device="cuda")
+    assert torch.equal(lru[0], ident) and torch.equal(tok[0], ident)        # L0 = 30 <= B: slot = position
+    assert np.array_equal(c.hot[0][0, :30].cpu().numpy(), c.host_np[0][0, :30])
+    for r in (1, 2, 3):                                                     # skipped, or not in the batch
+        assert torch.equal(lru[r], lru0[r]) and torch.equal(tok[r], tok0[r])
+    assert not c.hot[0][1:].any()
+    c.close()
+
+
 def test_corrupt_state_is_flagged_not_faulted():
     R, K, B = 2, 24, 64
     c = _cache(R=R, K=K, B=B)
