@@ -216,15 +216,18 @@ def test_replay_rejects_bad_plan_entries():
     c.close()
 
 
+@pytest.mark.parametrize("state", ["malloc", "static"])
 @pytest.mark.parametrize("form", ["separate", "fused"])
-def test_graph_capture_and_replay(form):
+def test_graph_capture_and_replay(form, state):
     """store_newest + swap_in + backup (three launches, or the one fused
     launch) captured once in a HIP graph, replayed step after step with new
     inputs copied into the captured buffers (eager work and synchronisation
-    between replays); every replay must equal the oracle's step."""
+    between replays); every replay must equal the oracle's step.  `static`:
+    the context from hisparse_init_static, whose state lives in the library's
+    static array (the callers that capture graphs are the ones it serves)."""
     R, B, K, rb = 6, 128, 40, 48
     max_seq = 1200
-    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq)
+    c = _cache(R=R, B=B, K=K, rb=rb, max_seq=max_seq, static_state=state == "static")
     o = _oracle_for(c)
     rng = np.random.default_rng(3)
     L = rng.integers(100, 900, size=R).astype(np.int32)
