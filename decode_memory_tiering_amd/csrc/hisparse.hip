@@ -1344,6 +1344,9 @@ int hisparse_init_static(const hisparse_config* cfg, hisparse_ctx** out)
         p += state;
     }
     c->in_scratch = true;
+    // Work a previous context queued on other streams (which need not wait for
+    // the null stream) may still use the array: let it finish first.
+    if (hipDeviceSynchronize() != hipSuccess) return HISPARSE_EHIP(hipGetLastError());
     rc = reset_state(c);   // the array keeps the last context's contents: every byte used is written here
     if (rc != HISPARSE_OK) return rc;
     slot.busy = true;

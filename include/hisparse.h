@@ -164,8 +164,10 @@ int hisparse_init(const hisparse_config* cfg, hisparse_ctx** out);
  * configuration that does not fit returns HISPARSE_ENOSPC.  One such context per device at a
  * time: while one is live (until hisparse_destroy), another call on that
  * device returns HISPARSE_EBUSY.  The array keeps the previous context's
- * contents, so this call writes every byte the new context uses (state as
- * after hisparse_init, error word 0), on the null stream, and waits for it.
+ * contents, so this call first waits for all work on the device (a destroyed
+ * context's last launches may still be running), then writes every byte the
+ * new context uses (state as after hisparse_init, error word 0) on the null
+ * stream, and waits for it.
  * Like hisparse_init it is a set-up call, made before any capture: it
  * launches on the null stream and waits.  Checks, limits and error codes are
  * otherwise those of hisparse_init, and every other call works on the
