@@ -203,6 +203,33 @@ def test_random_geometries(seed):
     _lockstep(wl, block_size=block, prefetch=bool(seed % 2), fuse_store=seed % 4 != 3)
 
 
+def _random_wide_workload(seed):
+    # larger batches and buffers than _random_workload: more requests per
+    # launch, wider rows of the LRU list per wave, long contexts, and the
+    # serving guide's 960-thread workgroup among the sizes
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(512, 8193))
+    K = int(rng.integers(1, min(B, 4096) + 1))
+    R = int(rng.integers(9, 65))
+    layers = int(rng.integers(1, 4))
+    anchor_of = tuple([0] + [0 if rng.random() < 0.5 else l for l in range(1, layers)])
+    paged = rng.random() < 0.3
+    kw = dict(page_size=int(rng.integers(8, 129)), resident_page_frac=float(rng.random() * 0.5)) if paged else \
+        dict(n_resident=int(rng.integers(0, R // 2 + 1)))
+    return W.Workload(f"fuzzwide{seed}", layers, anchor_of, R=R, B=B, K=K, rb=16 * int(rng.integers(1, 37)),
+                      steps=int(rng.integers(2, 5)), spec=int(rng.integers(1, 3)),
+                      topk_kind="mixture" if rng.random() < 0.6 else "uniform",
+                      seq_first=("uniform", B // 2, 3 * B), seed=6000 + seed, **kw)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_wide_geometries(seed):
+    wl = _random_wide_workload(seed)
+    blocks = [b for b in (256, 512, 960, 1024) if _launch_shape_fits(wl, b)]
+    block = blocks[seed % len(blocks)]
+    _lockstep(wl, block_size=block, prefetch=bool(seed % 2), fuse_store=seed % 4 != 3)
+
+
 def test_buffer_above_8192_slots():
     # the widest kernel instantiation (16 chunks of 64 slots per wave)
     wl = W.Workload("wide", 1, (0,), R=2, B=9000, K=3000, rb=16, steps=4, topk_kind="uniform",
