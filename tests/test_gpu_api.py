@@ -467,6 +467,79 @@ def test_page_copy_dma_parity():
         cc.close()
 
 
+def _random_transfers(rng, R, n_hp, n_src, n_mirror, mirror_frac):
+    """A transfer list with distinct destinations (host pages and mirror
+    pages), laid out in runs that are contiguous on every side as often as
+    not, so the runtime-copy form merges some and splits others."""
+    dest = [(r, hp) for r in range(R) for hp in range(n_hp)]
+    rng.shuffle(dest)
+    free_src = list(rng.permutation(n_src))
+    free_mirror = set(range(n_mirror))
+    out, used = [], set()
+    while dest and free_src:
+        r, hp = dest.pop()
+        if (r, hp) in used:
+            continue
+        run = int(rng.integers(1, 6))
+        sp = int(free_src.pop())
+        mp = -1
+        if free_mirror and rng.random() < mirror_frac:
+            mp = int(rng.choice(sorted(free_mirror)))
+        for j in range(run):
+            if (r, hp + j) in used or hp + j >= n_hp or sp + j >= n_src:
+                break
+            m = mp + j if mp >= 0 and (mp + j) in free_mirror else -1
+            if j and (m < 0) != (mp < 0):
+                break
+            out.append((sp + j, r, hp + j, m))
+            used.add((r, hp + j))
+            if m >= 0:
+                free_mirror.discard(m)
+            if sp + j in free_src:
+                free_src.remove(sp + j)
+    return np.array(out, np.int32).reshape(-1, 4)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_page_copy_random_lists(seed):
+    """Random spill and import lists (runs of 1-5 pages contiguous on every
+    side, scattered pages, mirrors, a last page cut at the pool end): the
+    runtime-copy form, the kernel form and the oracle agree byte for byte."""
+    rng = np.random.default_rng(900 + seed)
+    R = int(rng.integers(1, 6))
+    P = int(rng.choice([1, 7, 16, 64]))
+    rb = 16 * int(rng.integers(1, 9))
+    max_seq = int(rng.integers(2, 12)) * P - int(rng.integers(0, P))       # often a cut last page
+    n_hp = -(-max_seq // P)
+    n_src, n_mirror = int(rng.integers(4, 40)), int(rng.integers(0, 40))
+    src = rng.integers(0, 256, size=(n_src * P, rb), dtype=np.uint8)
+    spill = _random_transfers(rng, R, n_hp, n_src, 0, 0.0)
+    imp = _random_transfers(rng, R, n_hp, n_src, n_mirror, 0.5)
+    results = {}
+    o = None
+    for form in ("dma", "kernel"):
+        c = _cache(R=R, B=64, K=24, rb=rb, max_seq=max_seq)
+        o = o or _oracle_for(c)
+        src_d = _dev(src, torch.uint8)
+        mirror_d = torch.zeros(max(n_mirror, 1) * P, rb, dtype=torch.uint8, device="cuda")[: n_mirror * P]
+        if form == "dma":
+            c.spill_dma(0, src_d, P, spill)
+            c.import_pages_dma(0, src_d, P, mirror_d if n_mirror else None, imp)
+        else:
+            c.spill(0, src_d, P, _dev(spill))
+            c.import_pages(0, src_d, P, mirror_d if n_mirror else None, _dev(imp))
+        torch.cuda.synchronize()
+        assert c.get_error() == 0
+        results[form] = (c.host_np[0].copy(), mirror_d.cpu().numpy())
+        c.close()
+    mirror_np = np.zeros((n_mirror * P, rb), np.uint8)
+    o.page_copy(0, P, src, spill)
+    o.page_copy(0, P, src, imp, mirror=mirror_np if n_mirror else None)
+    for form, (host, mirror) in results.items():
+        assert np.array_equal(host, o.host[0]), form
+        assert np.array_equal(mirror, mirror_np), form
+
+
 def test_spill_mid_decode_round_trip():
     """A paged decode on GPU and oracle side by side; halfway, half of the
     resident pages are spilled and become host-backed; every output, state,
