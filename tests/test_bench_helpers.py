@@ -107,3 +107,16 @@ def test_cpu_baseline_reports_entries_and_copy_rate():
     assert got["threads"]["cores"] == min(2, len(__import__("os").sched_getaffinity(0)))
     assert got["copy_gbps"] == pytest.approx(got["value"] / entries * rows * wl.rb / 1e9)
     assert got["threads"]["copy_gbps"] == pytest.approx(got["threads"]["value"] / entries * rows * wl.rb / 1e9)
+
+
+def test_more_than_one_gpu_is_refused():
+    # one GPU only: asked for more, the benchmark says so and exits before
+    # touching any device
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120, cwd=root)
+    assert res.returncode == 2
+    assert "one GPU only" in res.stderr and res.stdout == ""
