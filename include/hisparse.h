@@ -62,8 +62,11 @@
  * corrupt state, a bad block-table entry) the affected batch row resolves to
  * all -1 with a plan count of 0 and leaves state and buffers untouched; the
  * per-request fast path and resident tier address no memory with top-k
- * entries and do not check them.  Replay, backup, spill and import skip the
- * offending row, pair or transfer and carry on with the rest.
+ * entries and do not check them.  Admission, replay, backup, spill and
+ * import skip the offending entry, row, pair or transfer and carry on with
+ * the rest; the runtime-copy forms of spill and import, whose transfer list
+ * is on the host, refuse a list with a bad transfer before issuing anything
+ * (HISPARSE_EINVAL).
  */
 #ifndef HISPARSE_H
 #define HISPARSE_H
