@@ -256,6 +256,15 @@ def test_batch_wider_than_the_replay_workgroup(prefetch):
     assert st["misses"] > 0
 
 
+def test_twelve_thousand_requests():
+    # a batch so wide that the replay's per-row prefix needs more than 64 KB
+    # of LDS (init raises the kernel's dynamic LDS limit for it)
+    wl = W.Workload("many_requests", 2, (0, 0), R=12000, B=16, K=8, rb=16, steps=3,
+                    seq_first=("uniform", 8, 60), seed=48)
+    st = _lockstep(wl)
+    assert st["misses"] > 0
+
+
 def test_million_token_context():
     # production inputs reach 1M tokens (HiCache page): positions past 2^20
     # through the hash, the slot map and the host-pool addressing
