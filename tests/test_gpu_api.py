@@ -750,6 +750,8 @@ def test_calls_reject_bad_layers_and_sizes():
         lambda: c.store_newest(0, rows[8:8 + 2 * c.rb], L),               # new rows not 16-byte aligned
         lambda: c.admit(1, torch.zeros(1, dtype=torch.int32, device="cuda"),
                         torch.ones(1, dtype=torch.int32, device="cuda")),  # admission is per anchor
+        lambda: c.get_state(1),                                             # a skip layer has no state
+        lambda: H.hisparse_set_stats(c.ctx, rows.data_ptr() + 4),          # counters not 8-byte aligned
     ]
     big = torch.zeros(5, c.K, dtype=torch.int32, device="cuda")           # 5 batch rows > 4 requests
     cases.append(lambda: c.swap_in(0, big, torch.full((5,), 10, dtype=torch.int32, device="cuda"), None, None,
